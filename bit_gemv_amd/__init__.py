@@ -1,0 +1,173 @@
+"""Python binding of librfp2 (ROCmFP2 GEMV / GEMM for MI355X).
+
+Argument marshalling only: every function here has the name and argument
+order of the C entry point declared in include/rfp2.h, takes torch tensors
+that live on the GPU, checks that each tensor has the dtype, layout and size
+the call will touch (so that no kernel reads or writes outside a buffer), and
+passes raw device pointers plus the current HIP stream to the library.  All
+computation happens in the library's HIP kernels; there is no fallback path:
+if librfp2.so is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librfp2.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "rfp2.h")
+
+RFP2_OK, RFP2_E_NULL, RFP2_E_SHAPE, RFP2_E_ALIGN, RFP2_E_LAUNCH = 0, -1, -2, -3, -4
+GEMV_MAX_M = 8
+
+_lib = None
+
+_c_i64 = ctypes.c_int64
+_c_p = ctypes.c_void_p
+_SIGNATURES = {
+    "rfp2_abi_version": ([], ctypes.c_int),
+    "rfp2_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "rfp2_quantize_acts": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p], ctypes.c_int),
+    "rfp2_quantize_weights": ([_c_p, _c_i64, _c_i64, _c_p, _c_p], ctypes.c_int),
+    "rfp2_gemv": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
+    "rfp2_gemm": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
+    "rfp2_moe_gemv": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p,
+                       _c_p, _c_p], ctypes.c_int),
+    "rfp2_debug_decode": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p], ctypes.c_int),
+    "rfp2_debug_half_dots": ([_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
+}
+
+
+class Rfp2Error(RuntimeError):
+    def __init__(self, call: str, status: int):
+        self.status = status
+        super().__init__(f"{call}: status {status}: {rfp2_status_string(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded librfp2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -c 'import "
+                "__graft_entry__ as g; g.build()'` (ROCm hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> list[str]:
+    """Names of the functions declared in include/rfp2.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(rfp2_\w+)\s*\(", text, re.M)))
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t, dtype, numel: int, name: str):
+    """Device pointer of `t` after checking what the call will touch."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {numel}")
+    return t.data_ptr()
+
+
+def _check(call: str, status: int):
+    if status != RFP2_OK:
+        raise Rfp2Error(call, status)
+
+
+def _blocks(K: int) -> int:
+    return K // 32
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names and argument order as the C ABI)
+# ---------------------------------------------------------------------------
+def rfp2_abi_version() -> int:
+    return lib().rfp2_abi_version()
+
+
+def rfp2_status_string(status: int) -> str:
+    return lib().rfp2_status_string(int(status)).decode()
+
+
+def rfp2_quantize_acts(a, M: int, K: int, q, d, stream=None) -> None:
+    import torch
+    _check("rfp2_quantize_acts", lib().rfp2_quantize_acts(
+        _ptr(a, torch.float32, M * K, "a"), M, K, _ptr(q, torch.int8, M * K, "q"),
+        _ptr(d, torch.float32, M * _blocks(K), "d"), _stream(stream)))
+
+
+def rfp2_quantize_weights(x, N: int, K: int, w, stream=None) -> None:
+    import torch
+    _check("rfp2_quantize_weights", lib().rfp2_quantize_weights(
+        _ptr(x, torch.float32, N * K, "x"), N, K,
+        _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), _stream(stream)))
+
+
+def rfp2_gemv(w, N: int, K: int, q, d, M: int, y, stream=None) -> None:
+    import torch
+    _check("rfp2_gemv", lib().rfp2_gemv(
+        _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), N, K,
+        _ptr(q, torch.int8, M * K, "q"), _ptr(d, torch.float32, M * _blocks(K), "d"), M,
+        _ptr(y, torch.float32, M * N, "y"), _stream(stream)))
+
+
+def rfp2_gemm(w, N: int, K: int, q, d, M: int, y, stream=None) -> None:
+    import torch
+    _check("rfp2_gemm", lib().rfp2_gemm(
+        _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), N, K,
+        _ptr(q, torch.int8, M * K, "q"), _ptr(d, torch.float32, M * _blocks(K), "d"), M,
+        _ptr(y, torch.float32, M * N, "y"), _stream(stream)))
+
+
+def rfp2_moe_gemv(w, E: int, N: int, K: int, ids, top_k: int, q, d, y, err=None,
+                  stream=None) -> None:
+    import torch
+    errp = None if err is None else _ptr(err, torch.int32, 1, "err")
+    _check("rfp2_moe_gemv", lib().rfp2_moe_gemv(
+        _ptr(w, torch.uint8, E * N * _blocks(K) * 10, "w"), E, N, K,
+        _ptr(ids, torch.int32, top_k, "ids"), top_k,
+        _ptr(q, torch.int8, K, "q"), _ptr(d, torch.float32, _blocks(K), "d"),
+        _ptr(y, torch.float32, top_k * N, "y"), errp, _stream(stream)))
+
+
+def rfp2_debug_decode(w, N: int, K: int, codes_out, scales_out, stream=None) -> None:
+    import torch
+    _check("rfp2_debug_decode", lib().rfp2_debug_decode(
+        _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), N, K,
+        _ptr(codes_out, torch.int8, N * K, "codes_out"),
+        _ptr(scales_out, torch.float32, N * K // 16, "scales_out"), _stream(stream)))
+
+
+def rfp2_debug_half_dots(w, N: int, K: int, q, M: int, sums_out, stream=None) -> None:
+    import torch
+    _check("rfp2_debug_half_dots", lib().rfp2_debug_half_dots(
+        _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), N, K,
+        _ptr(q, torch.int8, M * K, "q"), M,
+        _ptr(sums_out, torch.int32, M * N * _blocks(K) * 2, "sums_out"), _stream(stream)))

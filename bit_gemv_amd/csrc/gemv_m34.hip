@@ -1,0 +1,11 @@
+// Instantiations of the GEMV kernel for 3 and 4 activation columns.
+#include "gemv_kernel.h"
+
+namespace rfp2 {
+namespace gemv_detail {
+
+GemvFn pick_m3(int jt) { return pick_tile<3, false>(jt); }
+GemvFn pick_m4(int jt) { return pick_tile<4, false>(jt); }
+
+}  // namespace gemv_detail
+}  // namespace rfp2

@@ -1,0 +1,11 @@
+// Instantiations of the GEMV kernel for 5 and 6 activation columns.
+#include "gemv_kernel.h"
+
+namespace rfp2 {
+namespace gemv_detail {
+
+GemvFn pick_m5(int jt) { return pick_tile<5, false>(jt); }
+GemvFn pick_m6(int jt) { return pick_tile<6, false>(jt); }
+
+}  // namespace gemv_detail
+}  // namespace rfp2

@@ -1,0 +1,11 @@
+// Instantiations of the GEMV kernel for 7 and 8 activation columns.
+#include "gemv_kernel.h"
+
+namespace rfp2 {
+namespace gemv_detail {
+
+GemvFn pick_m7(int jt) { return pick_tile<7, false>(jt); }
+GemvFn pick_m8(int jt) { return pick_tile<8, false>(jt); }
+
+}  // namespace gemv_detail
+}  // namespace rfp2

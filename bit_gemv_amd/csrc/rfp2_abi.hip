@@ -1,0 +1,125 @@
+// C ABI of the library (declared in include/rfp2.h).  Every entry point checks
+// its arguments on the host and returns a status before anything is enqueued;
+// no HIP call is made for a rejected call.
+#include "rfp2.h"
+#include "rfp2_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxRows = int64_t(1) << 30;     // row and token counts
+constexpr int64_t kMaxGemvK = 32768;               // staged activations fit LDS
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+rfp2_status from_hip(hipError_t e) {
+  return e == hipSuccess ? RFP2_OK : RFP2_E_LAUNCH;
+}
+
+bool product_k_ok(int64_t K) {
+  return K >= 256 && K % 256 == 0 && K <= kMaxGemvK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rfp2_abi_version(void) { return RFP2_ABI_VERSION; }
+
+const char* rfp2_status_string(int status) {
+  switch (status) {
+    case RFP2_OK: return "ok";
+    case RFP2_E_NULL: return "a required pointer is null";
+    case RFP2_E_SHAPE: return "a size is out of range for this call";
+    case RFP2_E_ALIGN: return "a pointer is not aligned as this call requires";
+    case RFP2_E_LAUNCH: return "the HIP runtime reported an error for the launch";
+    default: return "unknown status";
+  }
+}
+
+rfp2_status rfp2_quantize_acts(const float* a, int64_t M, int64_t K, int8_t* q,
+                               float* d, hipStream_t stream) {
+  if (!a || !q || !d) return RFP2_E_NULL;
+  if (M < 1 || M > kMaxRows || K < 32 || K % 32 != 0 || K > (int64_t(1) << 30))
+    return RFP2_E_SHAPE;
+  if (!aligned(a, 16) || !aligned(q, 4) || !aligned(d, 4)) return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(rfp2::launch_quantize_acts(a, M, K, q, d, stream));
+}
+
+rfp2_status rfp2_quantize_weights(const float* x, int64_t N, int64_t K,
+                                  uint8_t* w, hipStream_t stream) {
+  if (!x || !w) return RFP2_E_NULL;
+  if (N < 1 || N > kMaxRows || K < 32 || K % 32 != 0 || K > (int64_t(1) << 30))
+    return RFP2_E_SHAPE;
+  if (!aligned(x, 4) || !aligned(w, 2)) return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(rfp2::launch_quantize_weights(x, N, K, w, stream));
+}
+
+rfp2_status rfp2_gemv(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
+                      const float* d, int64_t M, float* y, hipStream_t stream) {
+  if (!w || !q || !d || !y) return RFP2_E_NULL;
+  if (N < 1 || N > kMaxRows || M < 1 || M > RFP2_GEMV_MAX_M || !product_k_ok(K))
+    return RFP2_E_SHAPE;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(d, 4) || !aligned(y, 4))
+    return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(rfp2::launch_gemv(w, N, K, q, d, M, y, stream));
+}
+
+rfp2_status rfp2_gemm(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
+                      const float* d, int64_t M, float* y, hipStream_t stream) {
+  if (!w || !q || !d || !y) return RFP2_E_NULL;
+  if (N < 1 || N > kMaxRows || M < 1 || M > kMaxRows || K < 256 || K % 256 != 0 ||
+      K > (int64_t(1) << 24))
+    return RFP2_E_SHAPE;
+  if (((M + 127) / 128) * ((N + 127) / 128) > (int64_t(1) << 31) - 1)
+    return RFP2_E_SHAPE;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(d, 4) || !aligned(y, 4))
+    return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(rfp2::launch_gemm(w, N, K, q, d, M, y, stream));
+}
+
+rfp2_status rfp2_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                          const int32_t* ids, int64_t top_k, const int8_t* q,
+                          const float* d, float* y, int32_t* err,
+                          hipStream_t stream) {
+  if (!w || !ids || !q || !d || !y) return RFP2_E_NULL;
+  if (E < 1 || E > kMaxRows || N < 1 || N > kMaxRows || top_k < 1 ||
+      top_k > 65535 || !product_k_ok(K))
+    return RFP2_E_SHAPE;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(d, 4) || !aligned(y, 4) ||
+      !aligned(ids, 4) || (err && !aligned(err, 4)))
+    return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(rfp2::launch_moe_gemv(w, E, N, K, ids, top_k, q, d, y, err, stream));
+}
+
+rfp2_status rfp2_debug_decode(const uint8_t* w, int64_t N, int64_t K,
+                              int8_t* codes_out, float* scales_out,
+                              hipStream_t stream) {
+  if (!w || !codes_out || !scales_out) return RFP2_E_NULL;
+  if (N < 1 || N > kMaxRows || K < 32 || K % 32 != 0 || K > (int64_t(1) << 30))
+    return RFP2_E_SHAPE;
+  if (!aligned(w, 2) || !aligned(codes_out, 4) || !aligned(scales_out, 4))
+    return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(rfp2::launch_debug_decode(w, N, K, codes_out, scales_out, stream));
+}
+
+rfp2_status rfp2_debug_half_dots(const uint8_t* w, int64_t N, int64_t K,
+                                 const int8_t* q, int64_t M, int32_t* sums_out,
+                                 hipStream_t stream) {
+  if (!w || !q || !sums_out) return RFP2_E_NULL;
+  if (N < 1 || N > kMaxRows || M < 1 || M > kMaxRows || K < 32 || K % 32 != 0 ||
+      K > (int64_t(1) << 30))
+    return RFP2_E_SHAPE;
+  if (!aligned(w, 2) || !aligned(q, 4) || !aligned(sums_out, 4)) return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(rfp2::launch_debug_half_dots(w, N, K, q, M, sums_out, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// Launchers behind the C ABI.  Arguments have been validated by the caller
+// (rfp2_abi.hip); each launcher only sizes the grid and enqueues kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace rfp2 {
+
+constexpr int64_t kMaxGrid = 1 << 20;   // workgroups per launch (grid-stride beyond)
+
+hipError_t launch_quantize_acts(const float* a, int64_t M, int64_t K, int8_t* q,
+                                float* d, hipStream_t stream);
+hipError_t launch_quantize_weights(const float* x, int64_t N, int64_t K,
+                                   uint8_t* w, hipStream_t stream);
+hipError_t launch_gemv(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
+                       const float* d, int64_t M, float* y, hipStream_t stream);
+hipError_t launch_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                           const int32_t* ids, int64_t top_k, const int8_t* q,
+                           const float* d, float* y, int32_t* err,
+                           hipStream_t stream);
+hipError_t launch_gemm(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
+                       const float* d, int64_t M, float* y, hipStream_t stream);
+hipError_t launch_debug_decode(const uint8_t* w, int64_t N, int64_t K,
+                               int8_t* codes, float* scales, hipStream_t stream);
+hipError_t launch_debug_half_dots(const uint8_t* w, int64_t N, int64_t K,
+                                  const int8_t* q, int64_t M, int32_t* sums,
+                                  hipStream_t stream);
+
+}  // namespace rfp2

@@ -1,0 +1,159 @@
+/*
+ * rfp2.h -- C ABI of the ROCmFP2 GEMV / GEMM library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The format and the method follow the page "ROCmFP2 codebook research
+ * report" (llm.ciru.ai, 2026-07-13):
+ *
+ *   "01 · Storage": a block stores 32 weights in 10 bytes.  Bytes 0..7 are
+ *     code bytes; byte j holds weights 4j..4j+3, weight 4j+i in bits
+ *     2i..2i+1.  Byte 8 is the UE4M3 scale of weights 0..15, byte 9 the
+ *     scale of weights 16..31.  2.50 bits per weight.
+ *   "02 · Quantization": codes 00,01,10,11 mean -4,-1,+1,+4 times the scale
+ *     of their half.  A scale byte b (legal 0x00..0x7E) has E = b >> 3,
+ *     M = b & 7 and value M * 2^-10 (E == 0) or (8 + M) * 2^(E - 11).
+ *     The quantizer starts near max|x|/4, tries legal scales, maps all 16
+ *     values of the half to the nearest level (inner when |x/s| <= 2.5) and
+ *     keeps the scale with the least squared error.
+ *   "03 · Runtime": each code byte becomes four signed int8 lanes, which are
+ *     multiplied four at a time with int8 (Q8_1-style) activations and
+ *     accumulated in int32 per 16-weight half; the two weight scales and the
+ *     activation scale are applied after the integer sum,
+ *     d_a * (d_0 * S_0 + d_1 * S_1).  The multi-column kernel expands a
+ *     block once and reuses it for every activation column.
+ *
+ * Conventions shared by every entry point:
+ *   - Every data pointer is a DEVICE pointer owned by the caller (the library
+ *     allocates nothing, frees nothing and keeps no state between calls).
+ *   - Inputs are never written.  Outputs are overwritten, not accumulated.
+ *   - Every call only enqueues work on `stream` (0 = the null stream) and
+ *     returns; nothing is synchronised.  Calls are thread-safe.
+ *   - Matrices are row-major.  A stored weight matrix of N rows and K columns
+ *     is N rows of K/32 blocks, back to back: N * K / 32 * 10 bytes, row n at
+ *     byte n * K * 10 / 32.
+ *   - Activations are q int8 [M][K] plus d fp32 [M][K/32]: column (token) m
+ *     of the product uses q[m][k] * d[m][k/32].
+ *   - Argument errors are checked on the host before anything is enqueued;
+ *     the call then returns a negative status and launches nothing.
+ *   - Data errors are loud on the device: a scale byte outside 0x00..0x7E
+ *     makes every output that depends on it NaN.
+ */
+#ifndef RFP2_H
+#define RFP2_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rfp2_status {
+  RFP2_OK = 0,
+  RFP2_E_NULL = -1,   /* a required pointer is null                        */
+  RFP2_E_SHAPE = -2,  /* a size is out of range (see each call)            */
+  RFP2_E_ALIGN = -3,  /* a pointer is not aligned as the call requires     */
+  RFP2_E_LAUNCH = -4  /* the HIP runtime reported an error for the launch  */
+} rfp2_status;
+
+#define RFP2_ABI_VERSION 1
+#define RFP2_GEMV_MAX_M 8
+
+/* ABI version of the loaded library (RFP2_ABI_VERSION). */
+int rfp2_abi_version(void);
+
+/* Static English text for a status code; never NULL. */
+const char* rfp2_status_string(int status);
+
+/*
+ * rfp2_quantize_acts -- int8 activations, one fp32 scale per 32 values
+ * ("03 · Runtime": the int8 activation operand and its scale).
+ *   a  [M][K] fp32, 16-byte aligned.   q [M][K] int8, 4-byte aligned.
+ *   d  [M][K/32] fp32, 4-byte aligned.
+ * Per 32-value block: amax = max|a|, d = amax / 127 (IEEE fp32 division,
+ * round to nearest even), q = round(a / d) with halves away from zero,
+ * clamped to [-127, 127]; d == 0 gives q = 0.  A block holding a NaN or an
+ * infinity gets d = NaN and q = 0.
+ * Requires M >= 1, K >= 32, K % 32 == 0.
+ */
+rfp2_status rfp2_quantize_acts(const float* a, int64_t M, int64_t K,
+                               int8_t* q, float* d, hipStream_t stream);
+
+/*
+ * rfp2_quantize_weights -- pack fp32 weights into ROCmFP2 blocks
+ * ("02 · Quantization": how a block is chosen).
+ *   x [N][K] fp32, 4-byte aligned.  w [N * K/32 * 10] bytes, 2-byte aligned.
+ * Each 16-weight half gets the legal scale byte with the least squared
+ * reconstruction error over all 127 legal bytes (errors summed in fp64 in
+ * index order); on an exact tie the byte nearest to the start byte (the one
+ * whose scale is nearest max|x|/4, the lower on a tie) wins, the lower one
+ * first.  Codes: x < 0 negative, else positive; |x| <= 2.5 * s inner.
+ * Non-finite weights give unspecified bytes.
+ * Requires N >= 1, K >= 32, K % 32 == 0.
+ */
+rfp2_status rfp2_quantize_weights(const float* x, int64_t N, int64_t K,
+                                  uint8_t* w, hipStream_t stream);
+
+/*
+ * rfp2_gemv -- y[m][n] = sum_k w[n][k] * q[m][k] * d[m][k/32] for a few
+ * activation columns ("03 · Runtime": decode once, reuse for every column).
+ *   w [N][K/32][10] bytes, 16-byte aligned.  q [M][K] int8, 16-byte aligned.
+ *   d [M][K/32] fp32, 4-byte aligned.         y [M][N] fp32, 4-byte aligned.
+ * Requires N >= 1, 1 <= M <= RFP2_GEMV_MAX_M, 256 <= K <= 32768,
+ * K % 256 == 0 (a row is then a whole number of 80-byte groups and every row
+ * starts 16-byte aligned).
+ */
+rfp2_status rfp2_gemv(const uint8_t* w, int64_t N, int64_t K,
+                      const int8_t* q, const float* d, int64_t M,
+                      float* y, hipStream_t stream);
+
+/*
+ * rfp2_gemm -- the same product for a batch of M >= 1 activation columns
+ * (prompt batches), computed with i8 matrix-core instructions on int32
+ * per-half partials ("03 · Runtime" applied to a tile of columns).
+ * Layouts and alignment as rfp2_gemv.  Requires N >= 1, M >= 1,
+ * 256 <= K <= 2^24, K % 256 == 0.
+ */
+rfp2_status rfp2_gemm(const uint8_t* w, int64_t N, int64_t K,
+                      const int8_t* q, const float* d, int64_t M,
+                      float* y, hipStream_t stream);
+
+/*
+ * rfp2_moe_gemv -- routed-expert GEMV for one token.
+ *   w    E experts back to back, each [N][K/32][10] bytes; 16-byte aligned.
+ *   ids  [top_k] int32 on the device: the experts to apply, in output order.
+ *   q, d one activation column ([K] int8, [K/32] fp32).
+ *   y    [top_k][N] fp32: row j = expert ids[j] applied to the token.
+ *   err  nullable device int32: when an id lies outside [0, E) its row of y
+ *        is set to NaN and 1 is written to *err (never cleared by the call).
+ * Duplicate ids are legal.  Expert offsets are computed in 64 bits.
+ * Requires E >= 1, N >= 1, 1 <= top_k <= 65535, 256 <= K <= 32768,
+ * K % 256 == 0.
+ */
+rfp2_status rfp2_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                          const int32_t* ids, int64_t top_k,
+                          const int8_t* q, const float* d,
+                          float* y, int32_t* err, hipStream_t stream);
+
+/*
+ * Inspection entry points (they run the same device decode as the products).
+ *
+ * rfp2_debug_decode: the int8 lane each weight expands to and the fp32 scale
+ * of each half.  codes_out [N][K] int8, scales_out [N][K/16] fp32 (NaN for an
+ * illegal byte).  Requires N >= 1, K >= 32, K % 32 == 0; w 2-byte aligned.
+ *
+ * rfp2_debug_half_dots: the int32 sum of each 16-weight half against the int8
+ * activations, sums_out [M][N][K/32][2] int32.  Requires N >= 1, M >= 1,
+ * K >= 32, K % 32 == 0; w 2-byte aligned, q 4-byte aligned.
+ */
+rfp2_status rfp2_debug_decode(const uint8_t* w, int64_t N, int64_t K,
+                              int8_t* codes_out, float* scales_out,
+                              hipStream_t stream);
+rfp2_status rfp2_debug_half_dots(const uint8_t* w, int64_t N, int64_t K,
+                                 const int8_t* q, int64_t M,
+                                 int32_t* sums_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RFP2_H */
