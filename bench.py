@@ -10,10 +10,14 @@ quantized on the GPU (rfp2_quantize_weights) before timing, and the step
 rotates over enough distinct copies of them (>= 1 GiB in all) that every
 step reads its weights from HBM rather than from the 256 MB last-level cache.
 
-One JSON line is printed.  `value` is whole-job throughput (algorithmic bytes
-of the step / wall time of the step for GEMV workloads, 2*M*N*K / step time
-for the GEMM workload).  `roofline` describes the product kernel alone, from
-HIP events recorded around each of its launches on the bench stream.
+Timed steps are replayed from HIP graphs of up to 64 consecutive steps (each
+replay checked bit for bit against an eager step), so host launch cost does
+not set the pace.  One JSON line is printed.  `value` is whole-job
+throughput (algorithmic bytes of the step / wall time of the step for GEMV
+workloads, 2*M*N*K / step time for the GEMM workload).  `roofline` describes
+the product kernel alone: HIP events on the bench stream around graph
+replays of back-to-back launches of that kernel (so the average includes the
+gap between consecutive kernels).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -31,7 +35,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 I8_PEAK_TOPS = 5000.0          # MI355X dense int8 matrix cores, 5.0 POP/s
 COLD_BYTES = 1 << 30           # distinct weight bytes rotated through
-DEFAULT_WORKLOAD = "gemv_4096x4096"
+# The large-layer GEMV is the workload on which an HBM fraction is meaningful
+# (25 MiB of weights; the 5 MiB projection is latency-bound on this GPU).
+DEFAULT_WORKLOAD = "gemv_16384x5120"
+SECONDARY = ["gemv_4096x4096", "gemm_512x14336x4096"]
 KERNEL_SOURCES = ["rfp2_device.h", "gemv_kernel.h", "gemv.hip", "gemm.hip",
                   "quantize.hip"]
 
@@ -119,26 +126,13 @@ def cpu_baseline(cfg, budget_s: float = 12.0) -> dict:
     return out
 
 
-def main(argv=None) -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args(argv)
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the product kernels run on a single MI355X; no multi-GPU path exists)",
-              file=sys.stderr)
-        return 2
-
-    import numpy as np
+def measure(workload: str, steps: int, warmup: int) -> dict:
+    """Time one workload on cuda:0; returns the fields of its bench line."""
     import torch
     import bit_gemv_amd as rf
     import synth
 
-    cfg = dict(synth.WORKLOADS[args.workload], name=args.workload)
+    cfg = dict(synth.WORKLOADS[workload], name=workload)
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)
@@ -171,83 +165,139 @@ def main(argv=None) -> int:
         y = torch.empty((rows_out, N), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
 
-        def product(i):
+        def product(i, st):
             w = bank[i % copies]
             if cfg["op"] == "moe":
-                rf.rfp2_moe_gemv(w, cfg["E"], N, K, ids, cfg["top_k"], q, d, y, None, stream)
+                rf.rfp2_moe_gemv(w, cfg["E"], N, K, ids, cfg["top_k"], q, d, y, None, st)
             elif cfg["op"] == "gemm":
-                rf.rfp2_gemm(w, N, K, q, d, M, y, stream)
+                rf.rfp2_gemm(w, N, K, q, d, M, y, st)
             else:
-                rf.rfp2_gemv(w, N, K, q, d, M, y, stream)
+                rf.rfp2_gemv(w, N, K, q, d, M, y, st)
 
-        def step(i, ev=None):
-            rf.rfp2_quantize_acts(a, M, K, q, d, stream)
-            if ev is not None:
-                ev[0].record(stream)
-            product(i)
-            if ev is not None:
-                ev[1].record(stream)
+        def step(i, st):
+            rf.rfp2_quantize_acts(a, M, K, q, d, st)
+            product(i, st)
 
-        for i in range(args.warmup):
-            step(i)
+        # eager warm-up and the reference result of one step
+        for i in range(warmup):
+            step(i, stream)
+        step(0, stream)
         torch.cuda.synchronize()
+        y_eager = y.clone()
 
-        # whole-job timing (no per-kernel events inside)
+        # The timed loops are replayed from HIP graphs: one graph holds
+        # `per_graph` consecutive steps (weights rotating over the copies), so
+        # the host's launch cost does not set the pace.
+        per_graph = max(1, min(steps, copies, 64))
+        g_step = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step, stream=stream):
+            for i in range(per_graph):
+                step(i, stream)
+        g_prod = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_prod, stream=stream):
+            for i in range(per_graph):
+                product(per_graph + i, stream)
+        torch.cuda.synchronize()
+        # every replay must reproduce the eager result exactly (all weight
+        # copies are byte-identical)
+        for _ in range(3):
+            y.zero_()
+            torch.cuda.synchronize()
+            g_step.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(y, y_eager):
+                raise RuntimeError(f"{workload}: graph replay differs from the eager step")
+
+        reps = max(1, steps // per_graph)
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
+        g_step.replay()
         t_start.record(stream)
-        for i in range(args.steps):
-            step(args.warmup + i)
+        for _ in range(reps):
+            g_step.replay()
         t_end.record(stream)
         torch.cuda.synchronize()
-        ms_total = t_start.elapsed_time(t_end)
+        ms_step = t_start.elapsed_time(t_end) / (reps * per_graph)
 
-        # product-kernel timing: events around each launch on the same stream
-        n_ev = min(args.steps, 500)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n_ev)]
-        for i in range(n_ev):
-            step(i, evs[i])
+        # product kernel alone: events around replays of back-to-back launches
+        k_start = torch.cuda.Event(enable_timing=True)
+        k_end = torch.cuda.Event(enable_timing=True)
+        g_prod.replay()
+        k_start.record(stream)
+        for _ in range(reps):
+            g_prod.replay()
+        k_end.record(stream)
         torch.cuda.synchronize()
-        kern_ms = np.array([b.elapsed_time(e) for b, e in evs])
+        kern_ms = k_start.elapsed_time(k_end) / (reps * per_graph)
+        if not torch.equal(y, y_eager):
+            raise RuntimeError(f"{workload}: product graph result differs from the eager step")
+        del g_step, g_prod, bank, master
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
-    ms_step = ms_total / args.steps
-    kern_avg_s = float(np.mean(kern_ms)) * 1e-3
     khash = kernel_hash()
+    kernel = {"moe": "rfp2_moe_gemv", "gemm": "rfp2_gemm"}.get(cfg["op"], "rfp2_gemv")
     if cfg["op"] == "gemm":
         value = alg["ops"] / (ms_step * 1e-3) / 1e12
         unit, metric = "TOPS", "ROCmFP2 M=512 GEMM int8 TOPS"
-        achieved = alg["ops"] / kern_avg_s / 1e12
+        achieved = alg["ops"] / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": I8_PEAK_TOPS,
                 "unit": "TOPS", "frac": achieved / I8_PEAK_TOPS}
     else:
         value = (alg["quant_bytes"] + alg["product_bytes"]) / (ms_step * 1e-3) / 1e9
         unit, metric = "GB/s", "ROCmFP2 GEMV effective HBM GB/s"
-        achieved = alg["product_bytes"] / kern_avg_s / 1e9
+        achieved = alg["product_bytes"] / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS}
-    roof["traffic"] = traffic_from_profiles(args.workload, khash)
-    roof["kernel"] = {"moe": "rfp2_moe_gemv", "gemm": "rfp2_gemm"}.get(cfg["op"], "rfp2_gemv")
-    roof["kernel_us"] = {"mean": float(np.mean(kern_ms)) * 1e3,
-                         "p10": float(np.percentile(kern_ms, 10)) * 1e3,
-                         "p50": float(np.percentile(kern_ms, 50)) * 1e3,
-                         "p90": float(np.percentile(kern_ms, 90)) * 1e3}
-    roof["algorithmic_bytes"] = alg["product_bytes"]
+    roof.update(traffic=traffic_from_profiles(workload, khash), kernel=kernel,
+                kernel_us=kern_ms * 1e3, algorithmic_bytes=alg["product_bytes"],
+                algorithmic_ops=alg["ops"])
+    config = {"workload": workload, "M": M, "N": N, "K": K}
+    if cfg["op"] == "moe":
+        config.update(experts=cfg["E"], top_k=cfg["top_k"])
+    config.update(weight_copies=copies, weight_bytes_per_copy=per_copy,
+                  step="rfp2_quantize_acts + " + kernel, graph_steps=per_graph,
+                  kernel_hash=khash)
+    return {"metric": metric, "value": value, "unit": unit, "ms_per_step": ms_step,
+            "steps": reps * per_graph, "config": config, "roofline": roof, "cfg": cfg}
 
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--secondary", default=",".join(SECONDARY),
+                    help="comma-separated workloads also measured (empty: none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the product kernels run on a single MI355X; no multi-GPU path exists)",
+              file=sys.stderr)
+        return 2
+
+    r = measure(args.workload, args.steps, args.warmup)
     out = {
-        "metric": metric, "value": value, "unit": unit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "metric": r["metric"], "value": r["value"], "unit": r["unit"], "n_gpus": 1,
+        "steps": r["steps"], "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "i8", "data": "synthetic",
-        "config": {"workload": args.workload, "M": M, "N": N, "K": K,
-                   **({"experts": cfg["E"], "top_k": cfg["top_k"]} if cfg["op"] == "moe" else {}),
-                   "weight_copies": copies, "weight_bytes_per_copy": per_copy,
-                   "step": "rfp2_quantize_acts + " + roof["kernel"],
-                   "kernel_hash": khash},
-        "roofline": roof,
+        "dtype": "i8", "data": "synthetic", "config": r["config"],
+        "roofline": r["roofline"],
     }
+    secondary = []
+    for wl in [w for w in args.secondary.split(",") if w and w != args.workload]:
+        s = measure(wl, args.steps, args.warmup)
+        secondary.append({"workload": wl, "metric": s["metric"], "value": s["value"],
+                          "unit": s["unit"], "ms_per_step": s["ms_per_step"],
+                          "roofline": {k: s["roofline"][k] for k in
+                                       ("bound", "achieved", "peak", "unit", "frac",
+                                        "kernel", "kernel_us", "traffic")}})
+    if secondary:
+        out["secondary"] = secondary
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg)
+        out["cpu_baseline"] = cpu_baseline(r["cfg"])
     print(json.dumps(out), flush=True)
     return 0
 

@@ -11,19 +11,29 @@
 // gfx950 mapping
 //   * The stored matrix is one contiguous stream of 10-byte blocks.  K is a
 //     multiple of 256, so a row is a whole number of 80-byte groups (8 blocks,
-//     five 16-byte loads).  A lane owns whole groups: no block straddles two
-//     lanes and every load is a 16-byte vector load.
-//   * L lanes share a row, L being the largest power of two (<= 64) dividing
-//     the G = K/256 groups of a row; each lane takes J = G/L groups (group
-//     t + L*j for lane t).  A wave covers 64/L rows, so all 64 lanes work and
-//     the row sum is a log2(L)-step xor-shuffle reduction.
-//   * The loads of a lane's groups are issued before the workgroup stages the
-//     activations, so HBM latency overlaps the staging.
-//   * Activations are staged once per workgroup in LDS, transposed within
-//     each half to the lane order of the expanded weights (see expand_half),
-//     together with the per-block activation scales.  One 76-dword record per
-//     (column, group): 64 dwords of activations, 8 scales, 4 dwords of pad so
-//     that lanes reading neighbouring groups hit different LDS banks.
+//     five 16-byte pieces).  A lane owns whole groups: no block straddles two
+//     lanes.
+//   * A workgroup of wk waves computes S = 64/L rows.  Inside a wave, L lanes
+//     (a power of two) share a row; across the waves the row's G = K/256
+//     groups are split, so G = L * wk * J with J groups per lane (usually 1).
+//     Splitting K over waves, rather than giving one wave many groups per
+//     lane, keeps several waves per SIMD: while one wave decodes, the others'
+//     loads are in flight.  The row sum is a log2(L)-step xor shuffle inside
+//     the wave, then one LDS pass across the waves.
+//   * Weights move HBM -> LDS with direct loads (global_load_lds_dwordx4) in
+//     which consecutive lanes fetch consecutive 16-byte pieces, so every load
+//     instruction touches whole cache lines; each lane then reads its 80-byte
+//     group from LDS (conflict-free: lanes are 20 dwords apart).  Loading the
+//     80 bytes per lane straight into registers instead spreads each
+//     instruction over ~40 cache lines and was measured ~1.3x slower.
+//   * The first chunk of weights is requested before the wave stages its
+//     activations, so HBM latency overlaps the staging; the next chunk
+//     (J > 1) is requested as soon as the current one is in registers.
+//   * Each wave stages only the activations of its own groups in LDS,
+//     transposed within each half to the lane order of the expanded weights
+//     (see expand_half), with the per-block activation scales: one 76-dword
+//     record per (column, group): 64 dwords of activations, 8 scales and 4 of
+//     pad so that lanes reading neighbouring groups hit different banks.
 #include "gemv_kernel.h"
 
 namespace rfp2 {
@@ -56,42 +66,75 @@ GemvFn pick_kernel(int M, int jt) {
   }
 }
 
+constexpr int64_t kMinWorkgroups = 256;   // one per CU
+
 struct Geometry {
-  int lshift;   // log2 of lanes per row
+  int lshift;   // log2 of lanes per row inside a wave
+  int wk;       // waves per workgroup
   int J;        // groups per lane
-  int jt;       // groups per load tile (divides J)
-  int rows_per_wg;
+  int jt;       // chunks in flight per wave (divides J)
+  int rows;     // rows per workgroup
 };
 
-Geometry geometry(int64_t K) {
+// Choose how a row's G = K/256 groups are spread: G = L * wk * J.  Measured
+// on MI355X: one group per lane (J = 1, the most waves in flight) beats
+// deeper per-wave pipelining, and among J = 1 splits the one with the most
+// rows per workgroup (activation staging amortised over more rows) wins as
+// long as there is still a workgroup for every CU.
+Geometry geometry(int64_t K, int64_t rows_total) {
   const int G = (int)(K / 256);
-  int lshift = 0;
-  while (lshift < 6 && (G % (2 << lshift)) == 0) ++lshift;
-  Geometry g;
-  g.lshift = lshift;
-  g.J = G >> lshift;
-  g.jt = 1;
-  for (int c = kMaxGroupsPerTile; c >= 1; --c)
-    if (g.J % c == 0) { g.jt = c; break; }
-  g.rows_per_wg = kWaves * (64 >> lshift);
-  return g;
+  Geometry best{};
+  int64_t best_key = -1;
+  for (int ls = 0; ls <= 6; ++ls) {
+    const int L = 1 << ls;
+    if (G % L) continue;
+    const int rest = G / L;
+    for (int wk = std::min(rest, kMaxWaves); wk >= 1; --wk) {
+      if (rest % wk) continue;
+      const int J = rest / wk;
+      const int rows = 64 >> ls;
+      const int64_t wgs = (rows_total + rows - 1) / rows;
+      const int64_t enough = wgs >= kMinWorkgroups ? 1 : 0;
+      // key: fewer groups per lane first, then enough workgroups, then more
+      // rows per workgroup (or more workgroups when short of them)
+      const int64_t key = ((int64_t)(64 - std::min(J, 64)) << 40) | (enough << 39) |
+                          (enough ? (int64_t)rows << 20 : std::min<int64_t>(wgs, 1 << 19) << 20) |
+                          (int64_t)wk;
+      if (key > best_key) {
+        best_key = key;
+        best.lshift = ls;
+        best.wk = wk;
+        best.J = J;
+        best.rows = rows;
+      }
+      break;   // the largest wk for this L
+    }
+  }
+  best.jt = 1;
+  for (int c = kMaxChunksInFlight; c >= 1; --c)
+    if (best.J % c == 0) { best.jt = c; break; }
+  return best;
+}
+
+size_t lds_bytes(int M, const Geometry& g) {
+  const size_t per_wave = (size_t)g.jt * 1280 + (size_t)M * g.J * (1 << g.lshift) * kRecord;
+  return (g.wk * per_wave + (size_t)g.wk * g.rows * M) * 4;
 }
 
 }  // namespace
 
 hipError_t launch_gemv(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
                        const float* d, int64_t M, float* y, hipStream_t stream) {
-  const Geometry g = geometry(K);
-  const int G = (int)(K / 256);
-  const int per_col_lds = G * kRecord * 4;
-  const int cols_per_launch = std::max(1, std::min<int>((int)M, kMaxLdsBytes / per_col_lds));
-  const dim3 grid((uint32_t)((N + g.rows_per_wg - 1) / g.rows_per_wg));
-  for (int64_t m0 = 0; m0 < M; m0 += cols_per_launch) {
-    const int mc = (int)std::min<int64_t>(cols_per_launch, M - m0);
-    GemvFn fn = pick_kernel(mc, g.jt);
-    hipLaunchKernelGGL(fn, grid, dim3(256), (size_t)mc * per_col_lds, stream, w,
-                       (int)N, (int)K, q + m0 * K, d + m0 * (K / 32), y + m0 * N,
-                       g.lshift, g.J, (const int32_t*)nullptr, 0, (int32_t*)nullptr);
+  const Geometry g = geometry(K, N);
+  int cols = (int)M;
+  while (cols > 1 && lds_bytes(cols, g) > (size_t)kMaxLdsBytes) --cols;
+  const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows));
+  for (int64_t m0 = 0; m0 < M; m0 += cols) {
+    const int mc = (int)std::min<int64_t>(cols, M - m0);
+    Params p{w, (int)N, (int)K, q + m0 * K, d + m0 * (K / 32), y + m0 * N,
+             g.lshift, g.wk, g.J, nullptr, 0, nullptr};
+    hipLaunchKernelGGL(pick_kernel(mc, g.jt), grid, dim3(64 * g.wk), lds_bytes(mc, g),
+                       stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -102,12 +145,11 @@ hipError_t launch_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
                            const int32_t* ids, int64_t top_k, const int8_t* q,
                            const float* d, float* y, int32_t* err,
                            hipStream_t stream) {
-  const Geometry g = geometry(K);
-  const int G = (int)(K / 256);
-  const dim3 grid((uint32_t)((N + g.rows_per_wg - 1) / g.rows_per_wg), (uint32_t)top_k);
-  GemvFn fn = pick_tile<1, true>(g.jt);
-  hipLaunchKernelGGL(fn, grid, dim3(256), (size_t)G * kRecord * 4, stream, w,
-                     (int)N, (int)K, q, d, y, g.lshift, g.J, ids, (int)E, err);
+  const Geometry g = geometry(K, N * top_k);
+  const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows), (uint32_t)top_k);
+  Params p{w, (int)N, (int)K, q, d, y, g.lshift, g.wk, g.J, ids, (int)E, err};
+  const GemvFn fn = pick<1, true>(g.jt);
+  hipLaunchKernelGGL(fn, grid, dim3(64 * g.wk), lds_bytes(1, g), stream, p);
   return hipGetLastError();
 }
 

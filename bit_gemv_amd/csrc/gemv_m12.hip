@@ -4,8 +4,8 @@
 namespace rfp2 {
 namespace gemv_detail {
 
-GemvFn pick_m1(int jt) { return pick_tile<1, false>(jt); }
-GemvFn pick_m2(int jt) { return pick_tile<2, false>(jt); }
+GemvFn pick_m1(int jt) { return pick<1, false>(jt); }
+GemvFn pick_m2(int jt) { return pick<2, false>(jt); }
 
 }  // namespace gemv_detail
 }  // namespace rfp2

@@ -4,8 +4,8 @@
 namespace rfp2 {
 namespace gemv_detail {
 
-GemvFn pick_m3(int jt) { return pick_tile<3, false>(jt); }
-GemvFn pick_m4(int jt) { return pick_tile<4, false>(jt); }
+GemvFn pick_m3(int jt) { return pick<3, false>(jt); }
+GemvFn pick_m4(int jt) { return pick<4, false>(jt); }
 
 }  // namespace gemv_detail
 }  // namespace rfp2

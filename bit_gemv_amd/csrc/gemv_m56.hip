@@ -4,8 +4,8 @@
 namespace rfp2 {
 namespace gemv_detail {
 
-GemvFn pick_m5(int jt) { return pick_tile<5, false>(jt); }
-GemvFn pick_m6(int jt) { return pick_tile<6, false>(jt); }
+GemvFn pick_m5(int jt) { return pick<5, false>(jt); }
+GemvFn pick_m6(int jt) { return pick<6, false>(jt); }
 
 }  // namespace gemv_detail
 }  // namespace rfp2

@@ -4,8 +4,8 @@
 namespace rfp2 {
 namespace gemv_detail {
 
-GemvFn pick_m7(int jt) { return pick_tile<7, false>(jt); }
-GemvFn pick_m8(int jt) { return pick_tile<8, false>(jt); }
+GemvFn pick_m7(int jt) { return pick<7, false>(jt); }
+GemvFn pick_m8(int jt) { return pick<8, false>(jt); }
 
 }  // namespace gemv_detail
 }  // namespace rfp2

@@ -50,10 +50,19 @@ __device__ __forceinline__ void transpose_half(const uint32_t (&X)[4],
   A[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
 }
 
+// First dot of a chain: v_dot4_i32_i8 with an inline-constant zero
+// accumulator (the builtin with a zero accumulator becomes a v_mov of zero
+// plus the accumulating dot4c form: one extra VALU op per chain).
+__device__ __forceinline__ int32_t dot4_from_zero(uint32_t a, uint32_t b) {
+  int32_t r;
+  asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // int32 sum of one 16-weight half: four 4-lane int8 dot products.
 __device__ __forceinline__ int32_t half_dot(const uint32_t (&W)[4],
                                             const uint32_t* A) {
-  int32_t s = __builtin_amdgcn_sdot4((int)W[0], (int)A[0], 0, false);
+  int32_t s = dot4_from_zero(W[0], A[0]);
   s = __builtin_amdgcn_sdot4((int)W[1], (int)A[1], s, false);
   s = __builtin_amdgcn_sdot4((int)W[2], (int)A[2], s, false);
   s = __builtin_amdgcn_sdot4((int)W[3], (int)A[3], s, false);
