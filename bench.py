@@ -34,13 +34,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 I8_PEAK_TOPS = 5000.0          # MI355X dense int8 matrix cores, 5.0 POP/s
+F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16 matrix cores, 2.5 PFLOP/s
 COLD_BYTES = 1 << 30           # distinct weight bytes rotated through
 # The large-layer GEMV is the workload on which an HBM fraction is meaningful
 # (25 MiB of weights; the 5 MiB projection is latency-bound on this GPU).
 DEFAULT_WORKLOAD = "gemv_16384x5120"
-SECONDARY = ["gemv_4096x4096", "gemm_512x14336x4096"]
+SECONDARY = ["gemv_4096x4096", "gemm_512x14336x4096", "gemm_f16_512x14336x4096"]
 KERNEL_SOURCES = ["rfp2_device.h", "gemv_kernel.h", "gemv.hip", "gemm.hip",
-                  "quantize.hip"]
+                  "gemm_f16.hip", "quantize.hip"]
 
 
 def kernel_hash() -> str:
@@ -119,7 +120,7 @@ def cpu_baseline(cfg, budget_s: float = 12.0) -> dict:
     out = {"cores": int(blas_threads), "kind": "oracle",
            "sample": f"{rows} weight rows x {Mb} token(s) of {cfg['name']}, "
                      f"{reps} timed repetitions of quantize_acts + ref_gemv (fp64, numpy)"}
-    if cfg["op"] == "gemm":
+    if cfg["op"] in ("gemm", "gemm_f16"):
         out.update(value=sample_ops / per / 1e12, unit="TOPS")
     else:
         out.update(value=sample_bytes / per / 1e9, unit="GB/s")
@@ -171,6 +172,8 @@ def measure(workload: str, steps: int, warmup: int) -> dict:
                 rf.rfp2_moe_gemv(w, cfg["E"], N, K, ids, cfg["top_k"], q, d, y, None, st)
             elif cfg["op"] == "gemm":
                 rf.rfp2_gemm(w, N, K, q, d, M, y, st)
+            elif cfg["op"] == "gemm_f16":
+                rf.rfp2_gemm_f16(w, N, K, q, d, M, y, st)
             else:
                 rf.rfp2_gemv(w, N, K, q, d, M, y, st)
 
@@ -236,13 +239,16 @@ def measure(workload: str, steps: int, warmup: int) -> dict:
     torch.cuda.empty_cache()
 
     khash = kernel_hash()
-    kernel = {"moe": "rfp2_moe_gemv", "gemm": "rfp2_gemm"}.get(cfg["op"], "rfp2_gemv")
-    if cfg["op"] == "gemm":
+    kernel = {"moe": "rfp2_moe_gemv", "gemm": "rfp2_gemm",
+              "gemm_f16": "rfp2_gemm_f16"}.get(cfg["op"], "rfp2_gemv")
+    if cfg["op"] in ("gemm", "gemm_f16"):
         value = alg["ops"] / (ms_step * 1e-3) / 1e12
         unit, metric = "TOPS", "ROCmFP2 M=512 GEMM int8 TOPS"
         achieved = alg["ops"] / (kern_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": I8_PEAK_TOPS,
-                "unit": "TOPS", "frac": achieved / I8_PEAK_TOPS}
+        # the contraction's own dtype sets the peak: int8 5.0 POP/s, fp16 2.5 PFLOP/s
+        peak = I8_PEAK_TOPS if cfg["op"] == "gemm" else F16_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak,
+                "unit": "TOPS" if cfg["op"] == "gemm" else "TFLOP/s", "frac": achieved / peak}
     else:
         value = (alg["quant_bytes"] + alg["product_bytes"]) / (ms_step * 1e-3) / 1e9
         unit, metric = "GB/s", "ROCmFP2 GEMV effective HBM GB/s"

@@ -32,6 +32,7 @@ _SIGNATURES = {
     "rfp2_quantize_weights": ([_c_p, _c_i64, _c_i64, _c_p, _c_p], ctypes.c_int),
     "rfp2_gemv": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
     "rfp2_gemm": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
+    "rfp2_gemm_f16": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
     "rfp2_moe_gemv": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p,
                        _c_p, _c_p], ctypes.c_int),
     "rfp2_debug_decode": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p], ctypes.c_int),
@@ -141,6 +142,14 @@ def rfp2_gemv(w, N: int, K: int, q, d, M: int, y, stream=None) -> None:
 def rfp2_gemm(w, N: int, K: int, q, d, M: int, y, stream=None) -> None:
     import torch
     _check("rfp2_gemm", lib().rfp2_gemm(
+        _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), N, K,
+        _ptr(q, torch.int8, M * K, "q"), _ptr(d, torch.float32, M * _blocks(K), "d"), M,
+        _ptr(y, torch.float32, M * N, "y"), _stream(stream)))
+
+
+def rfp2_gemm_f16(w, N: int, K: int, q, d, M: int, y, stream=None) -> None:
+    import torch
+    _check("rfp2_gemm_f16", lib().rfp2_gemm_f16(
         _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), N, K,
         _ptr(q, torch.int8, M * K, "q"), _ptr(d, torch.float32, M * _blocks(K), "d"), M,
         _ptr(y, torch.float32, M * N, "y"), _stream(stream)))

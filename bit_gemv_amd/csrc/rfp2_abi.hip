@@ -83,6 +83,20 @@ rfp2_status rfp2_gemm(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
   return from_hip(rfp2::launch_gemm(w, N, K, q, d, M, y, stream));
 }
 
+rfp2_status rfp2_gemm_f16(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
+                          const float* d, int64_t M, float* y, hipStream_t stream) {
+  if (!w || !q || !d || !y) return RFP2_E_NULL;
+  if (N < 1 || N > kMaxRows || M < 1 || M > kMaxRows || K < 256 || K % 256 != 0 ||
+      K > (int64_t(1) << 24))
+    return RFP2_E_SHAPE;
+  if (((M + 127) / 128) * ((N + 127) / 128) > (int64_t(1) << 31) - 1)
+    return RFP2_E_SHAPE;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(d, 4) || !aligned(y, 4))
+    return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(rfp2::launch_gemm_f16(w, N, K, q, d, M, y, stream));
+}
+
 rfp2_status rfp2_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
                           const int32_t* ids, int64_t top_k, const int8_t* q,
                           const float* d, float* y, int32_t* err,

@@ -23,6 +23,8 @@ hipError_t launch_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
                            hipStream_t stream);
 hipError_t launch_gemm(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
                        const float* d, int64_t M, float* y, hipStream_t stream);
+hipError_t launch_gemm_f16(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
+                           const float* d, int64_t M, float* y, hipStream_t stream);
 hipError_t launch_debug_decode(const uint8_t* w, int64_t N, int64_t K,
                                int8_t* codes, float* scales, hipStream_t stream);
 hipError_t launch_debug_half_dots(const uint8_t* w, int64_t N, int64_t K,

@@ -119,6 +119,20 @@ rfp2_status rfp2_gemm(const uint8_t* w, int64_t N, int64_t K,
                       float* y, hipStream_t stream);
 
 /*
+ * rfp2_gemm_f16 -- the same product as rfp2_gemm, computed on the fp16
+ * matrix cores.  Every reconstructed weight (level x UE4M3 scale) and every
+ * int8 activation is exactly an fp16 number and every product is exact in
+ * fp32, so each 32-weight block's sum s0*S0 + s1*S1 comes out of the matrix
+ * core in fp32 (exact unless its two scales are more than 2^10 apart, where
+ * it rounds once) and only the activation scale is applied afterwards: one
+ * multiply-add per output and block instead of the int32 path's five.
+ * Layouts, alignment and limits as rfp2_gemm.
+ */
+rfp2_status rfp2_gemm_f16(const uint8_t* w, int64_t N, int64_t K,
+                          const int8_t* q, const float* d, int64_t M,
+                          float* y, hipStream_t stream);
+
+/*
  * rfp2_moe_gemv -- routed-expert GEMV for one token.
  *   w    E experts back to back, each [N][K/32][10] bytes; 16-byte aligned.
  *   ids  [top_k] int32 on the device: the experts to apply, in output order.

@@ -27,9 +27,11 @@ WORKLOADS = {
                             wseed=0),
     "gemv_16384x5120_m4": dict(op="gemv", M=4, N=16384, K=5120, sigma=0.015,
                                wseed=0),
-    # prompt-batch GEMM
+    # prompt-batch GEMM (int8 matrix cores; the same product on fp16 ones)
     "gemm_512x14336x4096": dict(op="gemm", M=512, N=14336, K=4096, sigma=0.02,
                                 wseed=0),
+    "gemm_f16_512x14336x4096": dict(op="gemm_f16", M=512, N=14336, K=4096,
+                                    sigma=0.02, wseed=0),
 }
 
 ACT_SEED = 1
