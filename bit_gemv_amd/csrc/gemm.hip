@@ -96,14 +96,15 @@ __device__ __forceinline__ void stage_to_lds(const Prefetch& f, Stage& st, int t
     *reinterpret_cast<uint2*>(dst) = make_uint2(W[0], W[1]);
     *reinterpret_cast<uint2*>(dst + 8) = make_uint2(W[2], W[3]);
   }
-  const float nan = __builtin_nanf("");
-  const bool bad0 = scale_flags_set<0>(scale_pair_bad<0>(f.wd[2]));
-  const bool bad1 = scale_flags_set<1>(scale_pair_bad<1>(f.wd[4]));
+  // an illegal scale byte in a block makes both of its scales NaN (bit-or
+  // with a quiet NaN pattern: no branch)
+  const uint32_t nan0 = scale_flags_set<0>(scale_pair_bad<0>(f.wd[2])) ? 0x7FC00000u : 0u;
+  const uint32_t nan1 = scale_flags_set<1>(scale_pair_bad<1>(f.wd[4])) ? 0x7FC00000u : 0u;
   float4 s;
-  s.x = bad0 ? nan : fp8_byte<0>(f.wd[2]);
-  s.y = bad0 ? nan : fp8_byte<1>(f.wd[2]);
-  s.z = bad1 ? nan : fp8_byte<2>(f.wd[4]);
-  s.w = bad1 ? nan : fp8_byte<3>(f.wd[4]);
+  s.x = __uint_as_float(__float_as_uint(fp8_byte<0>(f.wd[2])) | nan0);
+  s.y = __uint_as_float(__float_as_uint(fp8_byte<1>(f.wd[2])) | nan0);
+  s.z = __uint_as_float(__float_as_uint(fp8_byte<2>(f.wd[4])) | nan1);
+  s.w = __uint_as_float(__float_as_uint(fp8_byte<3>(f.wd[4])) | nan1);
   *reinterpret_cast<float4*>(&st.ws[wrow][4 * wpair]) = s;
 
   const int arow = tid >> 1, ahalf = tid & 1;

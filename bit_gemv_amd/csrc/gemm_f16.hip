@@ -57,7 +57,9 @@ struct PrefetchF16 {
 template <int BYTE>
 __device__ __forceinline__ void half_table(uint32_t word, bool bad, float fix,
                                            uint32_t& lo, uint32_t& hi) {
-  const float s = bad ? __builtin_nanf("") : fp8_byte<BYTE>(word) * fix;
+  // bit-or with a quiet NaN pattern instead of a select: no branch
+  const float s = __uint_as_float(__float_as_uint(fp8_byte<BYTE>(word) * fix) |
+                                  (bad ? 0x7FC00000u : 0u));
   const _Float16 h1 = (_Float16)s;
   const _Float16 h4 = (_Float16)(4.0f * s);
   const uint32_t b1 = __builtin_bit_cast(uint16_t, h1);
@@ -84,10 +86,19 @@ __device__ __forceinline__ void expand_half_f16(uint32_t X, uint32_t lo, uint32_
   }
 }
 
-__device__ __forceinline__ uint32_t pack_f16(int a, int b) {
-  const uint32_t x = __builtin_bit_cast(uint16_t, (_Float16)a);
-  const uint32_t y = __builtin_bit_cast(uint16_t, (_Float16)b);
-  return x | (y << 16);
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// Two int8 activations -> one dword of two exact fp16 values.  The byte
+// permute places a0 and a1 (raw two's-complement bytes) in the low byte of
+// each 16-bit lane; flipping bit 7 gives a + 128 in 0..255, and setting the
+// exponent bits 0x6400 makes that the fp16 number 1024 + a + 128 (fp16 has
+// unit spacing on [1024, 2048)); one packed subtraction of 1152 leaves a,
+// exactly.
+__device__ __forceinline__ uint32_t act_pair_f16(uint32_t X0, uint32_t X1, int j) {
+  const uint32_t sel = (uint32_t)j | (0x0Cu << 8) | ((uint32_t)(4 + j) << 16) | (0x0Cu << 24);
+  const uint32_t t = (__builtin_amdgcn_perm(X1, X0, sel) ^ 0x00800080u) | 0x64006400u;
+  const h2 v = __builtin_bit_cast(h2, t) - h2{(_Float16)1152.0f, (_Float16)1152.0f};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // 16 int8 activations of one half (natural order, 4 words) -> 8 dwords of
@@ -95,9 +106,8 @@ __device__ __forceinline__ uint32_t pack_f16(int a, int b) {
 __device__ __forceinline__ void act_half_f16(const uint32_t (&X)[4], uint32_t (&out)[8]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int s = 8 * j;
-    out[j] = pack_f16((int)(int8_t)(X[0] >> s), (int)(int8_t)(X[1] >> s));
-    out[4 + j] = pack_f16((int)(int8_t)(X[2] >> s), (int)(int8_t)(X[3] >> s));
+    out[j] = act_pair_f16(X[0], X[1], j);
+    out[4 + j] = act_pair_f16(X[2], X[3], j);
   }
 }
 
@@ -127,16 +137,12 @@ __device__ __forceinline__ void fetch(PrefetchF16& f, const uint8_t* __restrict_
 __device__ __forceinline__ void stage_to_lds(const PrefetchF16& f, StageF16& st, int tid,
                                              float fix) {
   const int wrow = tid >> 1, blk = tid & 1;
-  uint32_t c0, c1, sc;
-  if (blk == 0) {
-    c0 = f.wd[0];
-    c1 = f.wd[1];
-    sc = f.wd[2];
-  } else {
-    c0 = __builtin_amdgcn_alignbit(f.wd[3], f.wd[2], 16);
-    c1 = __builtin_amdgcn_alignbit(f.wd[4], f.wd[3], 16);
-    sc = f.wd[4] >> 16;
-  }
+  // block 0 of the pair is dwords 0..2 (scales in the low half of dword 2),
+  // block 1 starts 16 bits into dword 2; selects and funnel shifts, no branch
+  const uint32_t sh = 16u * (uint32_t)blk;
+  const uint32_t c0 = __builtin_amdgcn_alignbit(f.wd[3], blk ? f.wd[2] : f.wd[0], sh);
+  const uint32_t c1 = __builtin_amdgcn_alignbit(f.wd[4], blk ? f.wd[3] : f.wd[1], sh);
+  const uint32_t sc = (blk ? f.wd[4] : f.wd[2]) >> sh;
   const bool bad = scale_flags_set<0>(scale_pair_bad<0>(sc));
   uint32_t lo0, hi0, lo1, hi1;
   half_table<0>(sc, bad, fix, lo0, hi0);
@@ -163,6 +169,48 @@ __device__ __forceinline__ void stage_to_lds(const PrefetchF16& f, StageF16& st,
   st.ad[ablk][arow] = f.d;
 }
 
+// Block sums of the stage in sm for this wave's 64 x 64 (row x token) tile,
+// rescaled by the activation scales and added to acc.  MFMA operand A is the
+// weights (i = row), B the activations (j = token), so every lane holds one
+// token's column of each 32 x 32 tile and the activation scale of a block is
+// one register per tile.
+__device__ __forceinline__ void compute_stage(const StageF16& st, int lane, int wm, int wn,
+                                              v16f (&acc)[2][2]) {
+  const int koff = 16 * (lane >> 5);            // bytes: 8 fp16 per lane half
+#pragma unroll
+  for (int blk = 0; blk < BKB; ++blk) {
+    v8h a[2][2], b[2][2];                       // [half][tile]
+    float dd[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        a[h][t] = *reinterpret_cast<const v8h*>(
+            st.wh + (wn * 64 + t * 32 + (lane & 31)) * kRowBytes + blk * 64 + h * 32 + koff);
+        b[h][t] = *reinterpret_cast<const v8h*>(
+            st.ah + (wm * 64 + t * 32 + (lane & 31)) * kRowBytes + blk * 64 + h * 32 + koff);
+      }
+      dd[t] = st.ad[blk][wm * 64 + t * 32 + (lane & 31)];
+    }
+    // all four tiles' block sums first, then the rescale, so that the FMAs
+    // of a tile do not wait on the matrix-core latency of that same tile
+    v16f c[2][2];
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+      for (int tm = 0; tm < 2; ++tm) {
+        c[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[0][tn], b[0][tm], v16f{}, 0, 0, 0);
+        c[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[1][tn], b[1][tm], c[tn][tm], 0, 0, 0);
+      }
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+      for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[tn][tm][r] = fmaf(dd[tm], c[tn][tm][r], acc[tn][tm][r]);
+  }
+}
+
 __global__ __launch_bounds__(256, 2) void gemm_f16_kernel(
     const uint8_t* __restrict__ w, int N, int K, const int8_t* __restrict__ q,
     const float* __restrict__ d, int M, float* __restrict__ y, int m_tiles,
@@ -182,66 +230,55 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_kernel(
   const int stages = nb / BKB;
   const float fix = scale_fix();
 
-  v16f acc[2][2];
+  v16f acc[2][2];                               // [row tile][token tile]
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
 
+  // Software pipeline: iteration s computes stage s from one LDS buffer while
+  // it expands stage s+1 (already in registers) into the other buffer and
+  // loads stage s+2 from memory; a single barrier ends the iteration.  The
+  // buffer written in iteration s was last read in iteration s-1, before the
+  // barrier that ended it.  The loop body has no branch (the last stage is
+  // peeled off and the load of a stage past the end re-reads the last one),
+  // so the matrix-core and vector work of an iteration can be interleaved.
   PrefetchF16 f;
   fetch(f, w, q, d, row_bytes, K, nb, 0, tid, n0, m0, N, M);
-  const int koff = 16 * (lane >> 5);            // bytes: 8 fp16 per lane half
-  for (int s = 0; s < stages; ++s) {
-    StageF16& st = sm[s & 1];
-    stage_to_lds(f, st, tid, fix);
-    if (s + 1 < stages) fetch(f, w, q, d, row_bytes, K, nb, (s + 1) * BKB, tid, n0, m0, N, M);
+  stage_to_lds(f, sm[0], tid, fix);
+  fetch(f, w, q, d, row_bytes, K, nb, stages > 1 ? BKB : 0, tid, n0, m0, N, M);
+  __syncthreads();
+  for (int s = 0; s + 1 < stages; ++s) {
+    compute_stage(sm[s & 1], lane, wm, wn, acc);
+    stage_to_lds(f, sm[(s + 1) & 1], tid, fix);
+    const int next = s + 2 < stages ? s + 2 : stages - 1;
+    fetch(f, w, q, d, row_bytes, K, nb, next * BKB, tid, n0, m0, N, M);
     __syncthreads();
-
-#pragma unroll
-    for (int blk = 0; blk < BKB; ++blk) {
-      v8h a[2][2], b[2][2];                     // [half][tile]
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          a[h][t] = *reinterpret_cast<const v8h*>(
-              st.ah + (wm * 64 + t * 32 + (lane & 31)) * kRowBytes + blk * 64 + h * 32 + koff);
-          b[h][t] = *reinterpret_cast<const v8h*>(
-              st.wh + (wn * 64 + t * 32 + (lane & 31)) * kRowBytes + blk * 64 + h * 32 + koff);
-        }
-#pragma unroll
-      for (int tm = 0; tm < 2; ++tm) {
-        float dd[16];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const float4 dv = *reinterpret_cast<const float4*>(
-              &st.ad[blk][wm * 64 + tm * 32 + 8 * p + 4 * (lane >> 5)]);
-          dd[4 * p + 0] = dv.x;
-          dd[4 * p + 1] = dv.y;
-          dd[4 * p + 2] = dv.z;
-          dd[4 * p + 3] = dv.w;
-        }
-#pragma unroll
-        for (int tn = 0; tn < 2; ++tn) {
-          v16f c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[0][tm], b[0][tn], v16f{}, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[1][tm], b[1][tn], c, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[tm][tn][r] = fmaf(dd[r], c[r], acc[tm][tn][r]);
-        }
-      }
-    }
   }
+  compute_stage(sm[(stages - 1) & 1], lane, wm, wn, acc);
 
+  // lane -> token m, register r -> row n; rows n..n+3 of a register group are
+  // contiguous in y, so whole groups go out as one 16-byte store
+  const bool vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
 #pragma unroll
-  for (int tm = 0; tm < 2; ++tm)
+  for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn) {
-      const int n = n0 + wn * 64 + tn * 32 + (lane & 31);
-      if (n >= N) continue;
+    for (int tm = 0; tm < 2; ++tm) {
+      const int m = m0 + wm * 64 + tm * 32 + (lane & 31);
+      if (m >= M) continue;
+      float* yr = y + (int64_t)m * N;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + tm * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
-        if (m < M) y[(int64_t)m * N + n] = acc[tm][tn][r];
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * 64 + tn * 32 + 8 * g + 4 * (lane >> 5);
+        const v16f& v = acc[tn][tm];
+        if (vec && n + 3 < N) {
+          *reinterpret_cast<float4*>(yr + n) =
+              make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) yr[n + e] = v[4 * g + e];
+        }
       }
     }
 }

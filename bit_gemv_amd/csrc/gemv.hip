@@ -26,14 +26,19 @@
 //     group from LDS (conflict-free: lanes are 20 dwords apart).  Loading the
 //     80 bytes per lane straight into registers instead spreads each
 //     instruction over ~40 cache lines and was measured ~1.3x slower.
-//   * The first chunk of weights is requested before the wave stages its
-//     activations, so HBM latency overlaps the staging; the next chunk
-//     (J > 1) is requested as soon as the current one is in registers.
-//   * Each wave stages only the activations of its own groups in LDS,
-//     transposed within each half to the lane order of the expanded weights
-//     (see expand_half), with the per-block activation scales: one 76-dword
-//     record per (column, group): 64 dwords of activations, 8 scales and 4 of
-//     pad so that lanes reading neighbouring groups hit different banks.
+//   * Every global load is a direct-to-LDS load issued as inline asm, with
+//     explicit vmcnt waits: the activations of the wave's groups and their
+//     scales first (L2 hits), then the first chunk(s) of weights; the wave
+//     waits only for the activations, transposes them in place, and the
+//     weights keep streaming.  The next chunk (J > 1) is requested as soon as
+//     the current one is in registers.  (The compiler's own form of these
+//     loads makes it wait for all of them before any LDS access.)
+//   * Activations sit in LDS as 17 pieces of 16 bytes per (column, group):
+//     16 halves, each transposed to the lane order of the expanded weights
+//     (see expand_half), and one pad piece so that the lanes of a row, which
+//     read neighbouring groups, hit different banks.  The per-block scales
+//     sit in an array of their own.
+
 #include "gemv_kernel.h"
 
 namespace rfp2 {
@@ -116,8 +121,15 @@ Geometry geometry(int64_t K, int64_t rows_total) {
   return best;
 }
 
+// Per wave: jt chunk buffers, the activations (kGroupPieces 16-byte pieces
+// per column and group) and their scales, each rounded up to whole 64-lane
+// loads; then the cross-wave partial sums.  Must match the carving in
+// gemv_kernel.
 size_t lds_bytes(int M, const Geometry& g) {
-  const size_t per_wave = (size_t)g.jt * 1280 + (size_t)M * g.J * (1 << g.lshift) * kRecord;
+  const size_t ag = (size_t)g.J << g.lshift;
+  const size_t act_rounds = (M * ag * kGroupPieces + 63) / 64;
+  const size_t d_rounds = (M * ag * 8 + 63) / 64;
+  const size_t per_wave = (size_t)g.jt * 1280 + act_rounds * 256 + d_rounds * 64;
   return (g.wk * per_wave + (size_t)g.wk * g.rows * M) * 4;
 }
 

@@ -7,7 +7,11 @@
 namespace rfp2 {
 namespace gemv_detail {
 
-constexpr int kRecord = 76;          // LDS dwords per (column, 8-block group)
+// Activations of one (column, 8-block group) in LDS: 16 pieces of 16 bytes
+// (each the 16 int8 of one half, transposed) and one pad piece, so that the
+// L lanes of a row, which read L consecutive groups, hit different banks.
+constexpr int kGroupPieces = 17;
+constexpr int kGroupDwords = 4 * kGroupPieces;
 constexpr int kMaxLdsBytes = 65536;  // LDS budget per workgroup
 constexpr int kMaxWaves = 8;         // waves per workgroup (each owns a K slice)
 
@@ -26,11 +30,13 @@ struct Params {
 };
 
 // Decode one 80-byte group held in registers and accumulate its product with
-// M activation columns.  `act` points at the LDS record of column 0 for this
-// group; columns are `col_stride` dwords apart.
+// M activation columns.  `act` points at the LDS activations of column 0 for
+// this group and `dact` at its 8 block scales; columns are `act_stride` and
+// `d_stride` dwords apart.
 template <int M>
 __device__ __forceinline__ void group_product(const uint32_t (&dw)[20],
-                                              const uint32_t* act, int col_stride,
+                                              const uint32_t* act, int act_stride,
+                                              const float* dact, int d_stride,
                                               float (&acc)[M], uint32_t& bad_lo,
                                               uint32_t& bad_hi) {
 #pragma unroll
@@ -49,22 +55,22 @@ __device__ __forceinline__ void group_product(const uint32_t (&dw)[20],
     uint32_t W0[4], W1[4];
     expand_half(c0, W0);
     expand_half(c1, W1);
-    float s0, s1;
-    if ((jb & 1) == 0) {
-      s0 = fp8_byte<0>(sc);
-      s1 = fp8_byte<1>(sc);
-      bad_lo |= scale_pair_bad<0>(sc);
-    } else {
-      s0 = fp8_byte<2>(sc);
-      s1 = fp8_byte<3>(sc);
-      bad_hi |= scale_pair_bad<1>(sc);
-    }
+    // both scales of the block in one packed fp8 convert.  gfx950 converts
+    // OCP E4M3FN, where byte 0x7F is NaN: it poisons the row through the
+    // product.  Bytes 0x80..0xFF are caught by their top bits, OR-ed into
+    // bad_* (bits 7/15 for an even block, 23/31 for an odd one).
+    const float2 sp = (jb & 1) ? fp8_pair<true>(sc) : fp8_pair<false>(sc);
+    const float s0 = sp.x, s1 = sp.y;
+    if ((jb & 1) == 0)
+      bad_lo |= sc;
+    else
+      bad_hi |= sc;
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const uint32_t* a = act + m * col_stride + jb * 8;
+      const uint32_t* a = act + m * act_stride + jb * 8;
       const uint4 A0 = *reinterpret_cast<const uint4*>(a);
       const uint4 A1 = *reinterpret_cast<const uint4*>(a + 4);
-      const float dm = __uint_as_float(act[m * col_stride + 64 + jb]);
+      const float dm = dact[m * d_stride + jb];
       const uint32_t a0[4] = {A0.x, A0.y, A0.z, A0.w};
       const uint32_t a1[4] = {A1.x, A1.y, A1.z, A1.w};
       const int32_t S0 = half_dot(W0, a0);
@@ -104,20 +110,48 @@ __device__ __forceinline__ ChunkOffsets chunk_offsets(int lane, int lshift,
   return o;
 }
 
-__device__ __forceinline__ void load_chunk(const uint8_t* base, const ChunkOffsets& o,
-                                           uint32_t* dst) {
-#pragma unroll
-  for (int k = 0; k < 5; ++k)
-    __builtin_amdgcn_global_load_lds(base + o.off[k], dst + 256 * k, 16, 0, 0);
+// Direct-to-LDS loads, written as inline asm so that every wait on them is
+// the kernel's own: the compiler cannot tell which LDS bytes such a load
+// writes, so for its own form of the instruction it waits for all of them to
+// land before any LDS access and before using any earlier global load --
+// which would hold every weight read behind the activation staging and keep
+// the chunk ring from overlapping loads with compute.  Lane l of a 16-byte
+// load writes LDS bytes [m0 + 16 l, m0 + 16 l + 16); of a 4-byte load,
+// [m0 + 4 l, m0 + 4 l + 4).  m0 must be wave-uniform.  No global load in
+// this kernel is visible to the compiler, so it inserts no vmcnt wait of its
+// own; the s_nop covers the m0-write -> LDS-DMA hazard.  m0 is a register
+// the compiler reserves and sets right before each of its own uses (it
+// ignores it in a clobber list); nothing else in this kernel reads it.
+__device__ __forceinline__ void dma16(const void* src, uint32_t m0v) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(m0v) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t m0v) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(m0v) : "memory");
 }
 
-// Wait until at most 5*ahead weight loads (= `ahead` chunks) are outstanding.
+// Byte address of an LDS location (the form m0 takes), made wave-uniform.
+__device__ __forceinline__ uint32_t lds_m0(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+
+// One chunk: five 16-byte loads into the 5 KB at LDS byte address m0v.
+__device__ __forceinline__ void load_chunk(const uint8_t* base, const ChunkOffsets& o,
+                                           uint32_t m0v) {
+#pragma unroll
+  for (int k = 0; k < 5; ++k) dma16(base + o.off[k], m0v + 1024 * k);
+}
+
+// Wait until at most 5*ahead loads (= `ahead` chunks) are outstanding.
 __device__ __forceinline__ void wait_chunks(int ahead) {
   switch (ahead) {
     case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     case 1: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
     case 2: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
   }
 }
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -156,81 +190,79 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
   }
   wb += (int64_t)row0 * row_bytes;
 
-  // per-wave LDS: JT chunk buffers of 1280 dwords, then the activation
-  // records of this wave's groups (M columns x J*L groups)
+  // per-wave LDS: JT chunk buffers of 1280 dwords, then this wave's
+  // activations (M columns x ag = J*L groups of kGroupPieces pieces) and
+  // their block scales (8 per group), each rounded up to whole 64-lane loads
   const int ag = p.J << ls;                     // activation groups of the wave
-  const int wave_dwords = JT * 1280 + M * ag * kRecord;
+  const int n_pieces = M * ag * kGroupPieces;
+  const int n_scales = M * ag * 8;
+  const int act_rounds = (n_pieces + 63) >> 6;
+  const int d_rounds = (n_scales + 63) >> 6;
+  const int wave_dwords = JT * 1280 + act_rounds * 256 + d_rounds * 64;
   uint32_t* wlds = lds + wave * wave_dwords;
   uint32_t* alds = wlds + JT * 1280;
-  const int step = p.wk << ls;                  // groups between a wave's steps
-
-  // Activation loads go out first: they hit L2 and, since a wave's loads
-  // complete in issue order, queuing them behind the weights would hold the
-  // staging until the weights had arrived.  Item h = (column m, local group
-  // lgl = j*L + t', half b); its global group is (j*wk + wave)*L + t'.
-  const int n_halves = M * ag * 16;
-  const int n_scales = M * ag * 8;
+  float* dlds = reinterpret_cast<float*>(alds + act_rounds * 256);
   const int nb = K >> 5;
   auto group_of = [&](int lgl) {
     return (((lgl >> ls) * p.wk + wave) << ls) + (lgl & (L - 1));
   };
-  uint4 x0 = make_uint4(0u, 0u, 0u, 0u);
-  float d0 = 0.0f;
-  int rec0 = 0, drec0 = 0;
+
+  // The weight offsets are pure arithmetic: done first, they are ready when
+  // the loads go out.
+  const ChunkOffsets co = chunk_offsets(lane, ls, row0, N, row_bytes);
+
+  // The activations and their scales are loaded straight into place (they
+  // hit L2), then the first JT weight chunks.  Loads complete in issue order,
+  // so once no more than the 5*JT weight loads are outstanding the
+  // activations have landed.  LDS piece p holds piece p % 17 of local group
+  // g = p / 17 (column m = g / ag, local group lgl = g % ag, whose global
+  // group is (j*wk + wave)*L + t' for lgl = j*L + t'); pad pieces and the
+  // rounding slack re-read the first piece.
   {
-    const int m = M == 1 ? 0 : lane / (ag * 16);
-    const int r = lane - m * ag * 16;
-    const int lgl = r >> 4;
-    if (lane < n_halves) {
-      x0 = reinterpret_cast<const uint4*>(p.q + (int64_t)m * K)[group_of(lgl) * 16 + (r & 15)];
-      rec0 = (m * ag + lgl) * kRecord + ((r & 15) >> 1) * 8 + (r & 1) * 4;
+    const uint32_t m0 = lds_m0(alds);
+    for (int r = 0; r < act_rounds; ++r) {
+      const int pc = 64 * r + lane;
+      const int g = pc / kGroupPieces, piece = pc - g * kGroupPieces;
+      const int8_t* src = p.q;
+      if (piece < 16 && g < M * ag) {
+        const int m = M == 1 ? 0 : g / ag;
+        const int lgl = g - m * ag;
+        src = p.q + (int64_t)m * K + (int64_t)(group_of(lgl) * 16 + piece) * 16;
+      }
+      dma16(src, m0 + 1024 * r);
     }
-    const int md = M == 1 ? 0 : lane / (ag * 8);
-    const int rd = lane - md * ag * 8;
-    if (lane < n_scales) {
-      d0 = p.d[(int64_t)md * nb + group_of(rd >> 3) * 8 + (rd & 7)];
-      drec0 = (md * ag + (rd >> 3)) * kRecord + 64 + (rd & 7);
+    const uint32_t m0d = lds_m0(dlds);
+    for (int r = 0; r < d_rounds; ++r) {
+      const int i = min(64 * r + lane, n_scales - 1);
+      const int g = i >> 3;
+      const int m = M == 1 ? 0 : g / ag;
+      const int lgl = g - m * ag;
+      dma4(p.d + (int64_t)m * nb + group_of(lgl) * 8 + (i & 7), m0d + 256 * r);
     }
   }
-
-  // weights: the first JT chunks
-  const ChunkOffsets co = chunk_offsets(lane, ls, row0, N, row_bytes);
+  const uint32_t ring_m0 = lds_m0(wlds);
 #pragma unroll
   for (int j = 0; j < JT; ++j)                 // J is a multiple of JT
-    load_chunk(wb + (int64_t)((j * p.wk + wave) << ls) * 80, co, wlds + j * 1280);
+    load_chunk(wb + (int64_t)((j * p.wk + wave) << ls) * 80, co, ring_m0 + 5120 * j);
+  wait_chunks(JT);
 
-  // stage this wave's activations, transposed within each half
-  for (int h = lane; h < n_halves; h += 64) {
-    uint4 x = x0;
-    int rec = rec0;
-    if (h != lane) {
-      const int m = M == 1 ? 0 : h / (ag * 16);
-      const int r = h - m * ag * 16;
-      x = reinterpret_cast<const uint4*>(p.q + (int64_t)m * K)[group_of(r >> 4) * 16 + (r & 15)];
-      rec = (m * ag + (r >> 4)) * kRecord + ((r & 15) >> 1) * 8 + (r & 1) * 4;
-    }
+  // transpose each half's 16 activations in place into the lane order of
+  // the expanded weights
+  for (int pc = lane; pc < n_pieces; pc += 64) {
+    if (pc % kGroupPieces == 16) continue;
+    uint4* a = reinterpret_cast<uint4*>(alds) + pc;
+    const uint4 x = *a;
     const uint32_t X[4] = {x.x, x.y, x.z, x.w};
     uint32_t A[4];
     transpose_half(X, A);
-    *reinterpret_cast<uint4*>(alds + rec) = make_uint4(A[0], A[1], A[2], A[3]);
-  }
-  for (int i = lane; i < n_scales; i += 64) {
-    float v = d0;
-    int rec = drec0;
-    if (i != lane) {
-      const int m = M == 1 ? 0 : i / (ag * 8);
-      const int r = i - m * ag * 8;
-      v = p.d[(int64_t)m * nb + group_of(r >> 3) * 8 + (r & 7)];
-      rec = (m * ag + (r >> 3)) * kRecord + 64 + (r & 7);
-    }
-    alds[rec] = __float_as_uint(v);
+    *a = make_uint4(A[0], A[1], A[2], A[3]);
   }
 
   float acc[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
   uint32_t bad_lo = 0, bad_hi = 0;
-  const int col_stride = ag * kRecord;
+  const int act_stride = ag * kGroupDwords;
   for (int j = 0; j < p.J; ++j) {
     const int buf_i = JT == 1 ? 0 : j % JT;
     wait_chunks(min(JT, p.J - j) - 1);          // chunk j has landed
@@ -249,8 +281,10 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
     __builtin_amdgcn_wave_barrier();  // are staged: the buffer can be reused
     if (j + JT < p.J)
       load_chunk(wb + (int64_t)((((j + JT) * p.wk) + wave) << ls) * 80, co,
-                 wlds + buf_i * 1280);
-    group_product<M>(buf, alds + ((j << ls) + t) * kRecord, col_stride, acc, bad_lo, bad_hi);
+                 ring_m0 + 5120 * buf_i);
+    const int lgl = (j << ls) + t;
+    group_product<M>(buf, alds + lgl * kGroupDwords, act_stride, dlds + lgl * 8, ag * 8, acc,
+                     bad_lo, bad_hi);
   }
 
   // row sum: xor shuffles over the L lanes of the row, then over the waves

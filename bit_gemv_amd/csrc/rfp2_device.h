@@ -86,6 +86,14 @@ __device__ __forceinline__ float fp8_byte(uint32_t word) {
   return __builtin_amdgcn_cvt_f32_fp8((int)word, BYTE);
 }
 
+// Bytes 0,1 (HI = false) or 2,3 (HI = true) of `word` as two fp8 values.
+template <bool HI>
+__device__ __forceinline__ float2 fp8_pair(uint32_t word) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  const v2f v = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, HI);
+  return make_float2(v.x, v.y);
+}
+
 __device__ __forceinline__ float scale_fix() {
   return fp8_byte<0>(0x38u) > 0.75f ? 0.5f : 1.0f;
 }
