@@ -41,6 +41,8 @@
 
 #include "gemv_kernel.h"
 
+#include <cstdlib>
+
 namespace rfp2 {
 
 namespace gemv_detail {
@@ -71,8 +73,6 @@ GemvFn pick_kernel(int M, int jt) {
   }
 }
 
-constexpr int64_t kMinWorkgroups = 256;   // one per CU
-
 struct Geometry {
   int lshift;   // log2 of lanes per row inside a wave
   int wk;       // waves per workgroup
@@ -82,43 +82,51 @@ struct Geometry {
 };
 
 // Choose how a row's G = K/256 groups are spread: G = L * wk * J.  Measured
-// on MI355X: one group per lane (J = 1, the most waves in flight) beats
-// deeper per-wave pipelining, and among J = 1 splits the one with the most
-// rows per workgroup (activation staging amortised over more rows) wins as
-// long as there is still a workgroup for every CU.
-Geometry geometry(int64_t K, int64_t rows_total) {
+// on MI355X over every legal split (M = 1, 2, 4, 8; K = 2048..5120; 512 to
+// 16384 rows):
+//   * one group per lane for a single column (the most waves in flight);
+//     two for several columns (the decode and the per-lane set-up are shared
+//     by more products) when that still leaves >= 512 workgroups, else one;
+//     the nearest J when the target does not divide;
+//   * about four waves per workgroup (order 4, 5, 3, 6, 2, 8, 7, 1);
+//   * then the most rows per workgroup (activations shared by more rows);
+//   * one chunk in flight per wave: the next is requested as soon as the
+//     current one is in registers, and a deeper ring costs more LDS than it
+//     hides latency.
+constexpr int64_t kMinWorkgroupsForJ2 = 512;
+
+Geometry pick_geometry(int64_t K, int j_target) {
+  static constexpr int kWaveRank[kMaxWaves + 1] = {99, 7, 4, 2, 0, 1, 3, 6, 5};
   const int G = (int)(K / 256);
   Geometry best{};
-  int64_t best_key = -1;
+  int64_t best_key = INT64_MAX;
   for (int ls = 0; ls <= 6; ++ls) {
     const int L = 1 << ls;
     if (G % L) continue;
-    const int rest = G / L;
-    for (int wk = std::min(rest, kMaxWaves); wk >= 1; --wk) {
-      if (rest % wk) continue;
-      const int J = rest / wk;
-      const int rows = 64 >> ls;
-      const int64_t wgs = (rows_total + rows - 1) / rows;
-      const int64_t enough = wgs >= kMinWorkgroups ? 1 : 0;
-      // key: fewer groups per lane first, then enough workgroups, then more
-      // rows per workgroup (or more workgroups when short of them)
-      const int64_t key = ((int64_t)(64 - std::min(J, 64)) << 40) | (enough << 39) |
-                          (enough ? (int64_t)rows << 20 : std::min<int64_t>(wgs, 1 << 19) << 20) |
-                          (int64_t)wk;
-      if (key > best_key) {
+    for (int wk = 1; wk <= kMaxWaves; ++wk) {
+      if ((G / L) % wk) continue;
+      const int J = G / L / wk;
+      // smaller is better: distance from the target J (ties: fewer groups),
+      // then the wave-count rank, then fewer lanes per row (more rows)
+      const int64_t key = ((int64_t)std::abs(J - j_target) << 32) |
+                          ((int64_t)std::min(J, 0xFFFF) << 16) |
+                          ((int64_t)kWaveRank[wk] << 8) | ls;
+      if (key < best_key) {
         best_key = key;
-        best.lshift = ls;
-        best.wk = wk;
-        best.J = J;
-        best.rows = rows;
+        best = Geometry{ls, wk, J, 1, 64 >> ls};
       }
-      break;   // the largest wk for this L
     }
   }
-  best.jt = 1;
-  for (int c = kMaxChunksInFlight; c >= 1; --c)
-    if (best.J % c == 0) { best.jt = c; break; }
   return best;
+}
+
+// rows_total: the rows the launch covers (N, or N per expert times top_k)
+Geometry geometry(int64_t K, int64_t M, int64_t rows_total) {
+  if (M >= 2) {
+    const Geometry g = pick_geometry(K, 2);
+    if ((rows_total + g.rows - 1) / g.rows >= kMinWorkgroupsForJ2) return g;
+  }
+  return pick_geometry(K, 1);
 }
 
 // Per wave: jt chunk buffers, the activations (kGroupPieces 16-byte pieces
@@ -137,7 +145,7 @@ size_t lds_bytes(int M, const Geometry& g) {
 
 hipError_t launch_gemv(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
                        const float* d, int64_t M, float* y, hipStream_t stream) {
-  const Geometry g = geometry(K, N);
+  const Geometry g = geometry(K, M, N);
   int cols = (int)M;
   while (cols > 1 && lds_bytes(cols, g) > (size_t)kMaxLdsBytes) --cols;
   const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows));
@@ -157,7 +165,7 @@ hipError_t launch_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
                            const int32_t* ids, int64_t top_k, const int8_t* q,
                            const float* d, float* y, int32_t* err,
                            hipStream_t stream) {
-  const Geometry g = geometry(K, N * top_k);
+  const Geometry g = geometry(K, 1, N * top_k);
   const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows), (uint32_t)top_k);
   Params p{w, (int)N, (int)K, q, d, y, g.lshift, g.wk, g.J, ids, (int)E, err};
   const GemvFn fn = pick<1, true>(g.jt);

@@ -54,14 +54,21 @@ def test_gemv_shapes(N, K, M):
 
 
 def test_gemv_columns_are_independent():
+    # a column's result does not depend on the other columns of the call: a
+    # 4-column call and four 1-column calls agree to within twice the fp32
+    # bound (the split of K over lanes and waves, and so the summation order,
+    # is chosen per column count); a 4-column call repeated is bit-identical
     announce("gemv column independence")
     N, K = 200, 5120
     packed = random_blocks(N, K, seed=1, scale_hi=0x20)
     q, d = oracle.quantize_acts(synth.activations(4, K))
     y4 = run_gemv(packed, N, K, q, d)
+    assert np.array_equal(y4, run_gemv(packed, N, K, q, d))
+    absum = oracle.abs_product_sums(packed, N, K, q, d)
     for m in range(4):
         y1 = run_gemv(packed, N, K, q[m:m + 1], d[m:m + 1])
-        assert np.array_equal(y1[0], y4[m])
+        assert_within_bound(y4[m], y1[0].astype(np.float64), 2 * absum[m],
+                            f"column {m} alone vs in a batch of 4")
 
 
 def test_gemv_illegal_scale_gives_nan_row():
