@@ -122,13 +122,13 @@ __device__ __forceinline__ ChunkOffsets chunk_offsets(int lane, int lshift,
 // own; the s_nop covers the m0-write -> LDS-DMA hazard.  m0 is a register
 // the compiler reserves and sets right before each of its own uses (it
 // ignores it in a clobber list); nothing else in this kernel reads it.
-__device__ __forceinline__ void dma16(const void* src, uint32_t m0v) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(m0v) : "memory");
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t m0v) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(m0v) : "memory");
 }
-__device__ __forceinline__ void dma4(const void* src, uint32_t m0v) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(src), "s"(m0v) : "memory");
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t m0v) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(base), "s"(m0v) : "memory");
 }
 
 // Byte address of an LDS location (the form m0 takes), made wave-uniform.
@@ -141,7 +141,26 @@ __device__ __forceinline__ uint32_t lds_m0(const void* p) {
 __device__ __forceinline__ void load_chunk(const uint8_t* base, const ChunkOffsets& o,
                                            uint32_t m0v) {
 #pragma unroll
-  for (int k = 0; k < 5; ++k) dma16(base + o.off[k], m0v + 1024 * k);
+  for (int k = 0; k < 5; ++k) dma16(base, (uint32_t)o.off[k], m0v + 1024 * k);
+}
+
+// Sum of v over the L consecutive lanes of a row (L a power of two); every
+// lane of the row receives it.  Up to 16 lanes the steps are DPP moves fused
+// into the adds (quad permutes, then half-row and row mirrors: after each
+// step all lanes of a 2^i-lane group hold the same value, so a mirror adds
+// the partner group's sum); wider rows finish with cross-row shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_sum(float v, int L) {
+  if (L >= 2) v += dpp_move<0xB1>(v);     // quad_perm [1,0,3,2]
+  if (L >= 4) v += dpp_move<0x4E>(v);     // quad_perm [2,3,0,1]
+  if (L >= 8) v += dpp_move<0x141>(v);    // row_half_mirror
+  if (L >= 16) v += dpp_move<0x140>(v);   // row_mirror
+  if (L >= 32) v += __shfl_xor(v, 16, 64);
+  if (L >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
 }
 
 // Wait until at most 5*ahead loads (= `ahead` chunks) are outstanding.
@@ -172,7 +191,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
   const int ls = p.lshift;
   const int L = 1 << ls;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slot = lane >> ls;
   const int t = lane & (L - 1);
   const int row0 = blockIdx.x * (64 >> ls);
@@ -223,13 +242,13 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
     for (int r = 0; r < act_rounds; ++r) {
       const int pc = 64 * r + lane;
       const int g = pc / kGroupPieces, piece = pc - g * kGroupPieces;
-      const int8_t* src = p.q;
+      uint32_t off = 0;
       if (piece < 16 && g < M * ag) {
         const int m = M == 1 ? 0 : g / ag;
         const int lgl = g - m * ag;
-        src = p.q + (int64_t)m * K + (int64_t)(group_of(lgl) * 16 + piece) * 16;
+        off = (uint32_t)(m * K + (group_of(lgl) * 16 + piece) * 16);
       }
-      dma16(src, m0 + 1024 * r);
+      dma16(p.q, off, m0 + 1024 * r);
     }
     const uint32_t m0d = lds_m0(dlds);
     for (int r = 0; r < d_rounds; ++r) {
@@ -237,7 +256,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
       const int g = i >> 3;
       const int m = M == 1 ? 0 : g / ag;
       const int lgl = g - m * ag;
-      dma4(p.d + (int64_t)m * nb + group_of(lgl) * 8 + (i & 7), m0d + 256 * r);
+      dma4(p.d, (uint32_t)(4 * (m * nb + group_of(lgl) * 8 + (i & 7))), m0d + 256 * r);
     }
   }
   const uint32_t ring_m0 = lds_m0(wlds);
@@ -292,8 +311,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     float v = bad ? __builtin_nanf("") : acc[m];
-    for (int off = 1; off < L; off <<= 1) v += __shfl_xor(v, off, 64);
-    acc[m] = v;
+    acc[m] = row_sum(v, L);
   }
   const int S = 64 >> ls;
   if (p.wk > 1) {
