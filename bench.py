@@ -52,18 +52,29 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic(cfg) -> dict:
-    """Bytes the method must move (and int8 ops) per step, by workload."""
+def fused(cfg, two_launch: bool = False) -> bool:
+    """One-token workloads run as one launch that quantizes the activations
+    inside the product (rfp2_quant_gemv / rfp2_quant_moe_gemv)."""
+    return not two_launch and cfg["op"] in ("gemv", "moe") and cfg["M"] == 1
+
+
+def algorithmic(cfg, one_launch: bool = False) -> dict:
+    """Bytes the method must move (and int8 ops) per step, by workload.
+    Two launches: quantization (a in, q and d out), then the product (weights,
+    q and d in, y out).  One launch: weights and a in, q, d and y out."""
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
     w_row = K // 32 * 10
     quant = 4 * M * K + M * K + 4 * M * (K // 32)        # a in, q and d out
     if cfg["op"] == "moe":
         tk = cfg["top_k"]
-        prod = tk * N * w_row + K + 4 * (K // 32) + 4 * tk + 4 * tk * N
+        weights_y = tk * N * w_row + 4 * tk + 4 * tk * N
         ops = 2 * tk * N * K
     else:
-        prod = N * w_row + M * K + 4 * M * (K // 32) + 4 * M * N
+        weights_y = N * w_row + 4 * M * N
         ops = 2 * M * N * K
+    if one_launch:
+        return {"quant_bytes": 0, "product_bytes": weights_y + quant, "ops": ops}
+    prod = weights_y + M * K + 4 * M * (K // 32)
     return {"quant_bytes": quant, "product_bytes": prod, "ops": ops}
 
 
@@ -127,7 +138,7 @@ def cpu_baseline(cfg, budget_s: float = 12.0) -> dict:
     return out
 
 
-def measure(workload: str, steps: int, warmup: int) -> dict:
+def measure(workload: str, steps: int, warmup: int, two_launch: bool = False) -> dict:
     """Time one workload on cuda:0; returns the fields of its bench line."""
     import torch
     import bit_gemv_amd as rf
@@ -137,7 +148,8 @@ def measure(workload: str, steps: int, warmup: int) -> dict:
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)
-    alg = algorithmic(cfg)
+    one = fused(cfg, two_launch)
+    alg = algorithmic(cfg, one)
     w_row = K // 32 * 10
 
     with torch.cuda.stream(stream):
@@ -168,7 +180,12 @@ def measure(workload: str, steps: int, warmup: int) -> dict:
 
         def product(i, st):
             w = bank[i % copies]
-            if cfg["op"] == "moe":
+            if one and cfg["op"] == "moe":
+                rf.rfp2_quant_moe_gemv(w, cfg["E"], N, K, ids, cfg["top_k"], a, q, d, y, None,
+                                       st)
+            elif one:
+                rf.rfp2_quant_gemv(w, N, K, a, q, d, y, st)
+            elif cfg["op"] == "moe":
                 rf.rfp2_moe_gemv(w, cfg["E"], N, K, ids, cfg["top_k"], q, d, y, None, st)
             elif cfg["op"] == "gemm":
                 rf.rfp2_gemm(w, N, K, q, d, M, y, st)
@@ -178,7 +195,8 @@ def measure(workload: str, steps: int, warmup: int) -> dict:
                 rf.rfp2_gemv(w, N, K, q, d, M, y, st)
 
         def step(i, st):
-            rf.rfp2_quantize_acts(a, M, K, q, d, st)
+            if not one:
+                rf.rfp2_quantize_acts(a, M, K, q, d, st)
             product(i, st)
 
         # eager warm-up and the reference result of one step
@@ -241,6 +259,8 @@ def measure(workload: str, steps: int, warmup: int) -> dict:
     khash = kernel_hash()
     kernel = {"moe": "rfp2_moe_gemv", "gemm": "rfp2_gemm",
               "gemm_f16": "rfp2_gemm_f16"}.get(cfg["op"], "rfp2_gemv")
+    if one:
+        kernel = "rfp2_quant_moe_gemv" if cfg["op"] == "moe" else "rfp2_quant_gemv"
     if cfg["op"] in ("gemm", "gemm_f16"):
         value = alg["ops"] / (ms_step * 1e-3) / 1e12
         unit, metric = "TOPS", "ROCmFP2 M=512 GEMM int8 TOPS"
@@ -262,7 +282,8 @@ def measure(workload: str, steps: int, warmup: int) -> dict:
     if cfg["op"] == "moe":
         config.update(experts=cfg["E"], top_k=cfg["top_k"])
     config.update(weight_copies=copies, weight_bytes_per_copy=per_copy,
-                  step="rfp2_quantize_acts + " + kernel, graph_steps=per_graph,
+                  step=kernel if one else "rfp2_quantize_acts + " + kernel,
+                  graph_steps=per_graph,
                   kernel_hash=khash)
     return {"metric": metric, "value": value, "unit": unit, "ms_per_step": ms_step,
             "steps": reps * per_graph, "config": config, "roofline": roof, "cfg": cfg}
@@ -277,6 +298,9 @@ def main(argv=None) -> int:
     ap.add_argument("--secondary", default=",".join(SECONDARY),
                     help="comma-separated workloads also measured (empty: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--two-launch", action="store_true",
+                    help="one-token workloads as rfp2_quantize_acts + the product "
+                         "(default: the single quantizing launch)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -284,7 +308,7 @@ def main(argv=None) -> int:
               file=sys.stderr)
         return 2
 
-    r = measure(args.workload, args.steps, args.warmup)
+    r = measure(args.workload, args.steps, args.warmup, args.two_launch)
     out = {
         "metric": r["metric"], "value": r["value"], "unit": r["unit"], "n_gpus": 1,
         "steps": r["steps"], "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
@@ -294,7 +318,7 @@ def main(argv=None) -> int:
     }
     secondary = []
     for wl in [w for w in args.secondary.split(",") if w and w != args.workload]:
-        s = measure(wl, args.steps, args.warmup)
+        s = measure(wl, args.steps, args.warmup, args.two_launch)
         secondary.append({"workload": wl, "metric": s["metric"], "value": s["value"],
                           "unit": s["unit"], "ms_per_step": s["ms_per_step"],
                           "roofline": {k: s["roofline"][k] for k in

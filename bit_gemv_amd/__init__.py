@@ -35,6 +35,9 @@ _SIGNATURES = {
     "rfp2_gemm_f16": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
     "rfp2_moe_gemv": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p,
                        _c_p, _c_p], ctypes.c_int),
+    "rfp2_quant_gemv": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p], ctypes.c_int),
+    "rfp2_quant_moe_gemv": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p,
+                             _c_p, _c_p, _c_p], ctypes.c_int),
     "rfp2_debug_decode": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p], ctypes.c_int),
     "rfp2_debug_half_dots": ([_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
 }
@@ -163,6 +166,27 @@ def rfp2_moe_gemv(w, E: int, N: int, K: int, ids, top_k: int, q, d, y, err=None,
         _ptr(w, torch.uint8, E * N * _blocks(K) * 10, "w"), E, N, K,
         _ptr(ids, torch.int32, top_k, "ids"), top_k,
         _ptr(q, torch.int8, K, "q"), _ptr(d, torch.float32, _blocks(K), "d"),
+        _ptr(y, torch.float32, top_k * N, "y"), errp, _stream(stream)))
+
+
+def rfp2_quant_gemv(w, N: int, K: int, a, q, d, y, stream=None) -> None:
+    import torch
+    _check("rfp2_quant_gemv", lib().rfp2_quant_gemv(
+        _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), N, K,
+        _ptr(a, torch.float32, K, "a"), _ptr(q, torch.int8, K, "q"),
+        _ptr(d, torch.float32, _blocks(K), "d"), _ptr(y, torch.float32, N, "y"),
+        _stream(stream)))
+
+
+def rfp2_quant_moe_gemv(w, E: int, N: int, K: int, ids, top_k: int, a, q, d, y, err=None,
+                        stream=None) -> None:
+    import torch
+    errp = None if err is None else _ptr(err, torch.int32, 1, "err")
+    _check("rfp2_quant_moe_gemv", lib().rfp2_quant_moe_gemv(
+        _ptr(w, torch.uint8, E * N * _blocks(K) * 10, "w"), E, N, K,
+        _ptr(ids, torch.int32, top_k, "ids"), top_k,
+        _ptr(a, torch.float32, K, "a"), _ptr(q, torch.int8, K, "q"),
+        _ptr(d, torch.float32, _blocks(K), "d"),
         _ptr(y, torch.float32, top_k * N, "y"), errp, _stream(stream)))
 
 

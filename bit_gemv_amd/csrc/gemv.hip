@@ -152,7 +152,7 @@ hipError_t launch_gemv(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
   for (int64_t m0 = 0; m0 < M; m0 += cols) {
     const int mc = (int)std::min<int64_t>(cols, M - m0);
     Params p{w, (int)N, (int)K, q + m0 * K, d + m0 * (K / 32), y + m0 * N,
-             g.lshift, g.wk, g.J, nullptr, 0, nullptr};
+             g.lshift, g.wk, g.J, nullptr, 0, nullptr, nullptr, nullptr, nullptr};
     hipLaunchKernelGGL(pick_kernel(mc, g.jt), grid, dim3(64 * g.wk), lds_bytes(mc, g),
                        stream, p);
     const hipError_t e = hipGetLastError();
@@ -167,9 +167,48 @@ hipError_t launch_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
                            hipStream_t stream) {
   const Geometry g = geometry(K, 1, N * top_k);
   const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows), (uint32_t)top_k);
-  Params p{w, (int)N, (int)K, q, d, y, g.lshift, g.wk, g.J, ids, (int)E, err};
+  Params p{w, (int)N, (int)K, q, d, y, g.lshift, g.wk, g.J, ids, (int)E, err,
+           nullptr, nullptr, nullptr};
   const GemvFn fn = pick<1, true>(g.jt);
   hipLaunchKernelGGL(fn, grid, dim3(64 * g.wk), lds_bytes(1, g), stream, p);
+  return hipGetLastError();
+}
+
+// One token: quantize the activations inside the product kernel when every
+// wave's slice is at most 64 halves (J*L <= 4, which the one-column
+// geometry gives for K up to 8192 and beyond for most K), else the separate
+// quantization kernel followed by the product.  q and d are written either way.
+bool quant_fused(const Geometry& g) { return (g.J << g.lshift) <= 4 && g.jt == 1; }
+
+hipError_t launch_quant_gemv(const uint8_t* w, int64_t N, int64_t K, const float* a,
+                             int8_t* q, float* d, float* y, hipStream_t stream) {
+  const Geometry g = geometry(K, 1, N);
+  if (!quant_fused(g)) {
+    const hipError_t e = launch_quantize_acts(a, 1, K, q, d, stream);
+    if (e != hipSuccess) return e;
+    return launch_gemv(w, N, K, q, d, 1, y, stream);
+  }
+  const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows));
+  Params p{w, (int)N, (int)K, q, d, y, g.lshift, g.wk, g.J, nullptr, 0, nullptr, a, q, d};
+  hipLaunchKernelGGL((gemv_kernel<1, 1, false, true>), grid, dim3(64 * g.wk), lds_bytes(1, g),
+                     stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                                 const int32_t* ids, int64_t top_k, const float* a,
+                                 int8_t* q, float* d, float* y, int32_t* err,
+                                 hipStream_t stream) {
+  const Geometry g = geometry(K, 1, N * top_k);
+  if (!quant_fused(g)) {
+    const hipError_t e = launch_quantize_acts(a, 1, K, q, d, stream);
+    if (e != hipSuccess) return e;
+    return launch_moe_gemv(w, E, N, K, ids, top_k, q, d, y, err, stream);
+  }
+  const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows), (uint32_t)top_k);
+  Params p{w, (int)N, (int)K, q, d, y, g.lshift, g.wk, g.J, ids, (int)E, err, a, q, d};
+  hipLaunchKernelGGL((gemv_kernel<1, 1, true, true>), grid, dim3(64 * g.wk), lds_bytes(1, g),
+                     stream, p);
   return hipGetLastError();
 }
 

@@ -27,6 +27,9 @@ struct Params {
   const int32_t* ids;   // routed experts (MoE form) or null
   int E;
   int32_t* err;
+  const float* a;       // fp32 activations (quantizing form) or null
+  int8_t* qo;           // quantizing form: q and d written by workgroup 0
+  float* dout;
 };
 
 // Decode one 80-byte group held in registers and accumulate its product with
@@ -144,6 +147,98 @@ __device__ __forceinline__ void load_chunk(const uint8_t* base, const ChunkOffse
   for (int k = 0; k < 5; ++k) dma16(base, (uint32_t)o.off[k], m0v + 1024 * k);
 }
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Quantizing form: the lane's 16 fp32 activations (64 bytes at abase + aoff)
+// into registers, then one weight chunk (as load_chunk), then a wait for the
+// activations only.  One asm statement, so that the registers the loads fill
+// are not touched before the wait (the outputs are early-clobber: no input
+// shares a register with them while the loads are in flight).
+__device__ __forceinline__ void load_acts_and_chunk(const float* abase, uint32_t aoff,
+                                                    const uint8_t* wbase, const ChunkOffsets& o,
+                                                    uint32_t m0v, v4f (&x)[4]) {
+  asm volatile(
+      "global_load_dwordx4 %0, %4, %5\n\t"
+      "global_load_dwordx4 %1, %4, %5 offset:16\n\t"
+      "global_load_dwordx4 %2, %4, %5 offset:32\n\t"
+      "global_load_dwordx4 %3, %4, %5 offset:48\n\t"
+      "s_mov_b32 m0, %11\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, %12\n\t"
+      "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %7, %12\n\t"
+      "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %8, %12\n\t"
+      "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %9, %12\n\t"
+      "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %10, %12\n\t"
+      "s_waitcnt vmcnt(5)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+      : "v"(aoff), "s"(abase), "v"(o.off[0]), "v"(o.off[1]), "v"(o.off[2]), "v"(o.off[3]),
+        "v"(o.off[4]), "s"(m0v), "s"(wbase)
+      : "memory");
+}
+
+// Quantize the 16 fp32 activations of one half in place of the separate
+// activation kernel, with its exact arithmetic: the block's max |a| comes
+// from this lane and its partner (the other half of the block, lane ^ 1),
+// d = fl32(max / 127) (IEEE division), q = roundf(fl32(a / d)) (halves away
+// from zero), d = NaN and q = 0 for a block with a non-finite value, q = 0
+// when d = 0.  |a / d| <= 127 * (1 + 2^-23), so q never needs the clamp to
+// +-127.
+//   * fl32(a / d) is replaced by t = a * rcp(d) (rcp within one ulp), off by
+//     less than 2.7e-5 for |a / d| <= 127.5 whether or not the product is
+//     rounded before the next step (the compiler fuses it into the add);
+//     adding 1.5 * 2^23 rounds t to the nearest integer k and leaves k's
+//     two's-complement low byte in the low byte of the sum.  When
+//     |t - k| < 0.49997, k is roundf(fl32(a / d)) (fl32 adds at most 3.9e-6).
+//   * Otherwise (t within 3e-5 of a half-integer), or when d is subnormal,
+//     the lane redoes its values with the IEEE division and roundf.
+// X receives q packed four per dword in natural order; returns d.
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2,
+                                                   uint32_t b3) {
+  // v_perm: selector bytes 0..3 pick from the second source, 4..7 from the
+  // first, 0x0C gives zero
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x04000C0Cu);
+  return lo | hi;
+}
+
+__device__ __forceinline__ float quantize_half(const v4f (&x)[4], uint32_t (&X)[4]) {
+  constexpr float kMagic = 12582912.0f;          // 1.5 * 2^23
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[4 * i] = x[i].x;
+    v[4 * i + 1] = x[i].y;
+    v[4 * i + 2] = x[i].z;
+    v[4 * i + 3] = x[i].w;
+  }
+  // max |a| as the largest magnitude bit pattern: NaN and Inf sort above
+  // every finite value, so the same max decides finiteness
+  uint32_t amb = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amb = max(amb, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  amb = max(amb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amb, 0xB1, 0xF, 0xF, false));
+  X[0] = X[1] = X[2] = X[3] = 0u;
+  if (amb >= 0x7F800000u) return __builtin_nanf("");
+  const float dv = __fdiv_rn(__uint_as_float(amb), 127.0f);
+  if (dv == 0.0f) return dv;
+  const float inv = __builtin_amdgcn_rcpf(dv);
+  bool need_exact = dv < 1.17549435e-38f;
+  uint32_t u[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float t = v[i] * inv;
+    const float s = t + kMagic;                  // rounds t to an integer
+    need_exact |= fabsf(t - (s - kMagic)) > 0.49997f;
+    u[i] = __float_as_uint(s);
+  }
+  if (need_exact) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      u[i] = __float_as_uint(roundf(__fdiv_rn(v[i], dv)) + kMagic);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) X[i] = pack_low_bytes(u[4 * i], u[4 * i + 1], u[4 * i + 2], u[4 * i + 3]);
+  return dv;
+}
+
 // Sum of v over the L consecutive lanes of a row (L a power of two); every
 // lane of the row receives it.  Up to 16 lanes the steps are DPP moves fused
 // into the adds (quad permutes, then half-row and row mirrors: after each
@@ -184,8 +279,9 @@ __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)"
 // groups, so no workgroup barrier precedes the products; one barrier
 // precedes the final cross-wave sum.  M activation columns; MOE selects the
 // weight matrix through ids[blockIdx.y].
-template <int M, int JT, bool MOE>
+template <int M, int JT, bool MOE, bool QA>
 __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
+  static_assert(!QA || (M == 1 && JT == 1), "the quantizing form is one column, one chunk");
   extern __shared__ uint32_t lds[];
   const int K = p.K, N = p.N;
   const int ls = p.lshift;
@@ -230,51 +326,79 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
   // the loads go out.
   const ChunkOffsets co = chunk_offsets(lane, ls, row0, N, row_bytes);
 
-  // The activations and their scales are loaded straight into place (they
-  // hit L2), then the first JT weight chunks.  Loads complete in issue order,
-  // so once no more than the 5*JT weight loads are outstanding the
-  // activations have landed.  LDS piece p holds piece p % 17 of local group
-  // g = p / 17 (column m = g / ag, local group lgl = g % ag, whose global
-  // group is (j*wk + wave)*L + t' for lgl = j*L + t'); pad pieces and the
-  // rounding slack re-read the first piece.
-  {
-    const uint32_t m0 = lds_m0(alds);
-    for (int r = 0; r < act_rounds; ++r) {
-      const int pc = 64 * r + lane;
-      const int g = pc / kGroupPieces, piece = pc - g * kGroupPieces;
-      uint32_t off = 0;
-      if (piece < 16 && g < M * ag) {
+  const uint32_t ring_m0 = lds_m0(wlds);
+  if constexpr (QA) {
+    // Quantizing form: lane h of the wave takes half h of the wave's slice
+    // (ag*16 <= 64 halves; lanes past the end repeat the last one and write
+    // nothing), loads its fp32 activations and the weight chunk in one go,
+    // quantizes while the weights stream, and writes the int8 half
+    // (transposed) and the block scale to the same LDS slots the loaded
+    // form uses.  Workgroup 0 also writes q and d out.
+    const int n_halves = ag * 16;
+    const int h = min(lane, n_halves - 1);
+    const int lgl = h >> 4, piece = h & 15;
+    const int grp = group_of(lgl);
+    v4f x[4];
+    load_acts_and_chunk(p.a, (uint32_t)((grp * 256 + piece * 16) * 4),
+                        wb + (int64_t)(wave << ls) * 80, co, ring_m0, x);
+    uint32_t X[4];
+    const float dv = quantize_half(x, X);
+    if (lane < n_halves) {
+      uint32_t A[4];
+      transpose_half(X, A);
+      reinterpret_cast<uint4*>(alds)[lgl * kGroupPieces + piece] = make_uint4(A[0], A[1], A[2], A[3]);
+      if ((piece & 1) == 0) dlds[lgl * 8 + (piece >> 1)] = dv;
+      if (blockIdx.x == 0 && (!MOE || blockIdx.y == 0)) {
+        reinterpret_cast<uint4*>(p.qo)[grp * 16 + piece] = make_uint4(X[0], X[1], X[2], X[3]);
+        if ((piece & 1) == 0) p.dout[grp * 8 + (piece >> 1)] = dv;
+      }
+    }
+  } else {
+    // The activations and their scales are loaded straight into place (they
+    // hit L2), then the first JT weight chunks.  Loads complete in issue order,
+    // so once no more than the 5*JT weight loads are outstanding the
+    // activations have landed.  LDS piece p holds piece p % 17 of local group
+    // g = p / 17 (column m = g / ag, local group lgl = g % ag, whose global
+    // group is (j*wk + wave)*L + t' for lgl = j*L + t'); pad pieces and the
+    // rounding slack re-read the first piece.
+    {
+      const uint32_t m0 = lds_m0(alds);
+      for (int r = 0; r < act_rounds; ++r) {
+        const int pc = 64 * r + lane;
+        const int g = pc / kGroupPieces, piece = pc - g * kGroupPieces;
+        uint32_t off = 0;
+        if (piece < 16 && g < M * ag) {
+          const int m = M == 1 ? 0 : g / ag;
+          const int lgl = g - m * ag;
+          off = (uint32_t)(m * K + (group_of(lgl) * 16 + piece) * 16);
+        }
+        dma16(p.q, off, m0 + 1024 * r);
+      }
+      const uint32_t m0d = lds_m0(dlds);
+      for (int r = 0; r < d_rounds; ++r) {
+        const int i = min(64 * r + lane, n_scales - 1);
+        const int g = i >> 3;
         const int m = M == 1 ? 0 : g / ag;
         const int lgl = g - m * ag;
-        off = (uint32_t)(m * K + (group_of(lgl) * 16 + piece) * 16);
+        dma4(p.d, (uint32_t)(4 * (m * nb + group_of(lgl) * 8 + (i & 7))), m0d + 256 * r);
       }
-      dma16(p.q, off, m0 + 1024 * r);
     }
-    const uint32_t m0d = lds_m0(dlds);
-    for (int r = 0; r < d_rounds; ++r) {
-      const int i = min(64 * r + lane, n_scales - 1);
-      const int g = i >> 3;
-      const int m = M == 1 ? 0 : g / ag;
-      const int lgl = g - m * ag;
-      dma4(p.d, (uint32_t)(4 * (m * nb + group_of(lgl) * 8 + (i & 7))), m0d + 256 * r);
-    }
-  }
-  const uint32_t ring_m0 = lds_m0(wlds);
 #pragma unroll
-  for (int j = 0; j < JT; ++j)                 // J is a multiple of JT
-    load_chunk(wb + (int64_t)((j * p.wk + wave) << ls) * 80, co, ring_m0 + 5120 * j);
-  wait_chunks(JT);
+    for (int j = 0; j < JT; ++j)                 // J is a multiple of JT
+      load_chunk(wb + (int64_t)((j * p.wk + wave) << ls) * 80, co, ring_m0 + 5120 * j);
+    wait_chunks(JT);
 
-  // transpose each half's 16 activations in place into the lane order of
-  // the expanded weights
-  for (int pc = lane; pc < n_pieces; pc += 64) {
-    if (pc % kGroupPieces == 16) continue;
-    uint4* a = reinterpret_cast<uint4*>(alds) + pc;
-    const uint4 x = *a;
-    const uint32_t X[4] = {x.x, x.y, x.z, x.w};
-    uint32_t A[4];
-    transpose_half(X, A);
-    *a = make_uint4(A[0], A[1], A[2], A[3]);
+    // transpose each half's 16 activations in place into the lane order of
+    // the expanded weights
+    for (int pc = lane; pc < n_pieces; pc += 64) {
+      if (pc % kGroupPieces == 16) continue;
+      uint4* a = reinterpret_cast<uint4*>(alds) + pc;
+      const uint4 x = *a;
+      const uint32_t X[4] = {x.x, x.y, x.z, x.w};
+      uint32_t A[4];
+      transpose_half(X, A);
+      *a = make_uint4(A[0], A[1], A[2], A[3]);
+    }
   }
 
   float acc[M];
@@ -347,10 +471,10 @@ constexpr int kMaxChunksInFlight = 4;
 template <int M, bool MOE>
 GemvFn pick(int jt) {
   switch (jt) {
-    case 1: return gemv_kernel<M, 1, MOE>;
-    case 2: return gemv_kernel<M, 2, MOE>;
-    case 3: return gemv_kernel<M, 3, MOE>;
-    default: return gemv_kernel<M, 4, MOE>;
+    case 1: return gemv_kernel<M, 1, MOE, false>;
+    case 2: return gemv_kernel<M, 2, MOE, false>;
+    case 3: return gemv_kernel<M, 3, MOE, false>;
+    default: return gemv_kernel<M, 4, MOE, false>;
   }
 }
 

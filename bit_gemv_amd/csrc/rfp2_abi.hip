@@ -112,6 +112,33 @@ rfp2_status rfp2_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
   return from_hip(rfp2::launch_moe_gemv(w, E, N, K, ids, top_k, q, d, y, err, stream));
 }
 
+rfp2_status rfp2_quant_gemv(const uint8_t* w, int64_t N, int64_t K, const float* a,
+                            int8_t* q, float* d, float* y, hipStream_t stream) {
+  if (!w || !a || !q || !d || !y) return RFP2_E_NULL;
+  if (N < 1 || N > kMaxRows || !product_k_ok(K)) return RFP2_E_SHAPE;
+  if (!aligned(w, 16) || !aligned(a, 16) || !aligned(q, 16) || !aligned(d, 4) ||
+      !aligned(y, 4))
+    return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(rfp2::launch_quant_gemv(w, N, K, a, q, d, y, stream));
+}
+
+rfp2_status rfp2_quant_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                                const int32_t* ids, int64_t top_k, const float* a,
+                                int8_t* q, float* d, float* y, int32_t* err,
+                                hipStream_t stream) {
+  if (!w || !ids || !a || !q || !d || !y) return RFP2_E_NULL;
+  if (E < 1 || E > kMaxRows || N < 1 || N > kMaxRows || top_k < 1 ||
+      top_k > 65535 || !product_k_ok(K))
+    return RFP2_E_SHAPE;
+  if (!aligned(w, 16) || !aligned(a, 16) || !aligned(q, 16) || !aligned(d, 4) ||
+      !aligned(y, 4) || !aligned(ids, 4) || (err && !aligned(err, 4)))
+    return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(
+      rfp2::launch_quant_moe_gemv(w, E, N, K, ids, top_k, a, q, d, y, err, stream));
+}
+
 rfp2_status rfp2_debug_decode(const uint8_t* w, int64_t N, int64_t K,
                               int8_t* codes_out, float* scales_out,
                               hipStream_t stream) {

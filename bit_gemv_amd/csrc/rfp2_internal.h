@@ -21,6 +21,12 @@ hipError_t launch_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
                            const int32_t* ids, int64_t top_k, const int8_t* q,
                            const float* d, float* y, int32_t* err,
                            hipStream_t stream);
+hipError_t launch_quant_gemv(const uint8_t* w, int64_t N, int64_t K, const float* a,
+                             int8_t* q, float* d, float* y, hipStream_t stream);
+hipError_t launch_quant_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                                 const int32_t* ids, int64_t top_k, const float* a,
+                                 int8_t* q, float* d, float* y, int32_t* err,
+                                 hipStream_t stream);
 hipError_t launch_gemm(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
                        const float* d, int64_t M, float* y, hipStream_t stream);
 hipError_t launch_gemm_f16(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,

@@ -150,6 +150,35 @@ rfp2_status rfp2_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
                           float* y, int32_t* err, hipStream_t stream);
 
 /*
+ * rfp2_quant_gemv -- one token end to end: quantizes the fp32 activations a
+ * exactly as rfp2_quantize_acts does, writing q and d, and computes
+ * y = W * a as rfp2_gemv does from that q and d ("03 · Runtime": the int8
+ * activation operand, its scale, then the product), in a single kernel
+ * launch for most K: each wave quantizes the activations it needs while its
+ * weights stream in.  y, q and d are bit-identical to rfp2_quantize_acts
+ * followed by rfp2_gemv with M = 1.
+ *   w [N][K/32][10] bytes, 16-byte aligned.   a [K] fp32, 16-byte aligned.
+ *   q [K] int8, 16-byte aligned (written).     d [K/32] fp32, 4-byte aligned
+ *   (written).                                 y [N] fp32, 4-byte aligned.
+ * Requires N >= 1, 256 <= K <= 32768, K % 256 == 0.
+ */
+rfp2_status rfp2_quant_gemv(const uint8_t* w, int64_t N, int64_t K, const float* a,
+                            int8_t* q, float* d, float* y, hipStream_t stream);
+
+/*
+ * rfp2_quant_moe_gemv -- the routed-expert GEMV of rfp2_moe_gemv for one
+ * token given in fp32, with the activation quantization of
+ * rfp2_quantize_acts done inside the product launch (as rfp2_quant_gemv).
+ * w, ids, y, err and the limits as rfp2_moe_gemv; a, q, d as
+ * rfp2_quant_gemv.  y, q and d are bit-identical to rfp2_quantize_acts
+ * followed by rfp2_moe_gemv.
+ */
+rfp2_status rfp2_quant_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                                const int32_t* ids, int64_t top_k, const float* a,
+                                int8_t* q, float* d, float* y, int32_t* err,
+                                hipStream_t stream);
+
+/*
  * Inspection entry points (they run the same device decode as the products).
  *
  * rfp2_debug_decode: the int8 lane each weight expands to and the fp32 scale
