@@ -27,6 +27,16 @@ R7  Activations: per 32-element block, amax = max|a|, d = fl32(amax/127)
     When d == 0 (amax == 0, or amax so small that amax/127 underflows)
     every q of the block is 0.  Non-finite activations are rejected.
 R8  Rows are stored back to back, each row being K/32 blocks back to back.
+R14 Importance-weighted search ("05 · Completed experiment"): the error of a
+    candidate is sum_i w_i * (x_i - xhat_i)^2 with w_i = importance of the
+    value's input channel * sqrt(sigma^2 + x_i^2).  The page leaves sigma
+    undefined; here sigma^2 is the mean of x^2 over the 16-value half being
+    searched (the unit the search works on).  Each term is w * (e*e), summed
+    in index order, every step rounded once; the weights are computed once
+    per half (x*x summed in index order, /16, + x_i*x_i, sqrt, * importance).
+    The codes stay the nearest levels (a positive weight does not move a
+    value's nearest level); only the winning scale changes.  All-zero
+    importance makes every candidate score 0: the start byte wins.
 """
 from __future__ import annotations
 
@@ -184,8 +194,24 @@ def _visit_offsets():
         yield k
 
 
-def _search_halves(X: np.ndarray):
-    """Scale search on H halves at once.  X: fp64 [H,16].  -> (bytes, codes)."""
+def importance_weights(X: np.ndarray, IMP: np.ndarray) -> np.ndarray:
+    """Per-value weights of the importance-weighted objective ("05 · Completed
+    experiment": importance_i * sqrt(sigma^2 + x_i^2)), fp64 [H,16].
+
+    X: fp64 [H,16] halves; IMP: fp64 [H,16] importance of each value's input
+    channel.  sigma^2 is the mean of x^2 over the half (R14), summed in index
+    order; every step rounds once (x*x, sum, /16, +, sqrt, *)."""
+    s2 = np.zeros(X.shape[0])
+    for i in range(HALF_WEIGHTS):
+        s2 = s2 + X[:, i] * X[:, i]
+    sigma2 = s2 / 16.0
+    return IMP * np.sqrt(sigma2[:, None] + X * X)
+
+
+def _search_halves(X: np.ndarray, WT: np.ndarray | None = None):
+    """Scale search on H halves at once.  X: fp64 [H,16].  WT: per-value
+    weights of the objective (None: the plain squared error).
+    -> (bytes, codes)."""
     H = X.shape[0]
     table = ue4m3_table()
     start = start_byte(np.abs(X).max(axis=1))
@@ -201,7 +227,10 @@ def _search_halves(X: np.ndarray):
         sse = np.zeros(H)
         for i in range(HALF_WEIGHTS):                      # R6: index order
             e = X[:, i] - xhat[:, i]
-            sse = sse + e * e
+            t = e * e
+            if WT is not None:
+                t = WT[:, i] * t                           # weighted: w * (e*e)
+            sse = sse + t
         better = legal & (sse < best_sse)                  # R1: strictly lower
         best_sse[better] = sse[better]
         best_b[better] = b[better]
@@ -209,17 +238,37 @@ def _search_halves(X: np.ndarray):
     return best_b.astype(np.uint8), codes.astype(np.uint8)
 
 
-def quantize_half(x) -> tuple[int, list[int]]:
-    """Choose the scale byte and the 16 codes of one 16-weight half."""
+def _check_importance(imp, K: int) -> np.ndarray:
+    imp = np.asarray(imp)
+    if imp.dtype != np.float32 or imp.shape != (K,):
+        raise TypeError(f"importance must be float32 [{K}]")
+    if not (np.isfinite(imp).all() and (imp >= 0).all()):
+        raise ValueError("importance must be finite and >= 0")
+    return imp.astype(np.float64)
+
+
+def quantize_half(x, importance=None) -> tuple[int, list[int]]:
+    """Choose the scale byte and the 16 codes of one 16-weight half; with an
+    importance vector (fp32 [16], >= 0) the error is the weighted one."""
     X = np.asarray(x, dtype=np.float32).astype(np.float64).reshape(1, HALF_WEIGHTS)
     if not np.isfinite(X).all():
         raise ValueError("non-finite weight")
-    b, c = _search_halves(X)
+    WT = None
+    if importance is not None:
+        IMP = _check_importance(importance, HALF_WEIGHTS).reshape(1, HALF_WEIGHTS)
+        WT = importance_weights(X, IMP)
+    b, c = _search_halves(X, WT)
     return int(b[0]), [int(v) for v in c[0]]
 
 
-def quantize_weights(W: np.ndarray) -> np.ndarray:
-    """fp32 [N,K] -> packed ROCmFP2 bytes [N, 10K/32] (scale search per half)."""
+def quantize_weights(W: np.ndarray, importance=None) -> np.ndarray:
+    """fp32 [N,K] -> packed ROCmFP2 bytes [N, 10K/32] (scale search per half).
+
+    importance: None (plain squared error, "02 · Quantization") or fp32 [K],
+    finite and >= 0, the importance of each input channel (column); the
+    search then minimises the weighted error of "05 · Completed experiment".
+    The codes are the nearest levels either way; only the scale choice
+    changes."""
     W = np.asarray(W)
     if W.dtype != np.float32:
         raise TypeError("weights must be float32")
@@ -228,7 +277,12 @@ def quantize_weights(W: np.ndarray) -> np.ndarray:
     X = W.astype(np.float64).reshape(-1, HALF_WEIGHTS)
     if not np.isfinite(X).all():
         raise ValueError("non-finite weight")
-    ebytes, codes = _search_halves(X)
+    WT = None
+    if importance is not None:
+        imp = _check_importance(importance, K)
+        IMP = np.broadcast_to(imp.reshape(1, K), (N, K)).reshape(-1, HALF_WEIGHTS)
+        WT = importance_weights(X, IMP)
+    ebytes, codes = _search_halves(X, WT)
     return pack_matrix(codes.reshape(N, K), ebytes.reshape(N, K // HALF_WEIGHTS))
 
 
