@@ -138,6 +138,52 @@ def cpu_baseline(cfg, budget_s: float = 12.0) -> dict:
     return out
 
 
+def measure_quantizer(workload: str, reps: int = 5) -> dict:
+    """Weight-quantizer throughput on the workload's matrix: the plain and
+    the importance-weighted scale search on the GPU (weights per second,
+    graph-free back-to-back launches between events), and the CPU oracle on
+    a 16-row sample of the same matrix."""
+    import numpy as np
+    import torch
+    import bit_gemv_amd as rf
+    import oracle
+    import synth
+
+    cfg = synth.WORKLOADS[workload]
+    N, K = cfg["N"], cfg["K"]
+    dev = torch.device("cuda:0")
+    W = synth.weights(N, K, cfg["sigma"], seed=cfg["wseed"])
+    imp = synth.importance(K)
+    x = torch.from_numpy(W).to(dev)
+    imp_g = torch.from_numpy(imp).to(dev)
+    w = torch.empty(N * K // 32 * 10, dtype=torch.uint8, device=dev)
+    out = {"workload": workload, "weights": N * K}
+    for name, call in (("plain", lambda: rf.rfp2_quantize_weights(x, N, K, w)),
+                       ("imatrix", lambda: rf.rfp2_quantize_weights_imatrix(x, N, K, imp_g, w))):
+        call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[f"gpu_{name}_ms"] = ms
+        out[f"gpu_{name}_gweights_per_s"] = N * K / (ms * 1e-3) / 1e9
+    rows = 16
+    t0 = time.perf_counter()
+    oracle.quantize_weights(W[:rows])
+    t_plain = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.quantize_weights(W[:rows], imp)
+    t_imp = time.perf_counter() - t0
+    out.update(cpu_oracle_plain_mweights_per_s=rows * K / t_plain / 1e6,
+               cpu_oracle_imatrix_mweights_per_s=rows * K / t_imp / 1e6,
+               cpu_sample=f"{rows} rows of {workload}, numpy fp64, one thread for the search")
+    return out
+
+
 def measure(workload: str, steps: int, warmup: int, two_launch: bool = False) -> dict:
     """Time one workload on cuda:0; returns the fields of its bench line."""
     import torch
@@ -298,6 +344,8 @@ def main(argv=None) -> int:
     ap.add_argument("--secondary", default=",".join(SECONDARY),
                     help="comma-separated workloads also measured (empty: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quantizer", action="store_true",
+                    help="also time the weight quantizers (plain and importance-weighted)")
     ap.add_argument("--two-launch", action="store_true",
                     help="one-token workloads as rfp2_quantize_acts + the product "
                          "(default: the single quantizing launch)")
@@ -328,6 +376,8 @@ def main(argv=None) -> int:
         out["secondary"] = secondary
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(r["cfg"])
+    if args.quantizer:
+        out["weight_quantizer"] = measure_quantizer(args.workload)
     print(json.dumps(out), flush=True)
     return 0
 

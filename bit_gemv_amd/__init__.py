@@ -30,6 +30,7 @@ _SIGNATURES = {
     "rfp2_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "rfp2_quantize_acts": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p], ctypes.c_int),
     "rfp2_quantize_weights": ([_c_p, _c_i64, _c_i64, _c_p, _c_p], ctypes.c_int),
+    "rfp2_quantize_weights_imatrix": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p], ctypes.c_int),
     "rfp2_gemv": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
     "rfp2_gemm": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
     "rfp2_gemm_f16": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
@@ -131,6 +132,14 @@ def rfp2_quantize_weights(x, N: int, K: int, w, stream=None) -> None:
     import torch
     _check("rfp2_quantize_weights", lib().rfp2_quantize_weights(
         _ptr(x, torch.float32, N * K, "x"), N, K,
+        _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), _stream(stream)))
+
+
+def rfp2_quantize_weights_imatrix(x, N: int, K: int, importance, w, stream=None) -> None:
+    import torch
+    _check("rfp2_quantize_weights_imatrix", lib().rfp2_quantize_weights_imatrix(
+        _ptr(x, torch.float32, N * K, "x"), N, K,
+        _ptr(importance, torch.float32, K, "importance"),
         _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), _stream(stream)))
 
 

@@ -68,7 +68,16 @@ hipError_t launch_quantize_acts(const float* a, int64_t M, int64_t K, int8_t* q,
 // among equal errors the byte nearest the start byte (nearest scale to
 // max|x|/4, lower on a tie), lower side first.
 // ---------------------------------------------------------------------------
-__device__ void search_half(const float* x, uint32_t& code_word, uint32_t& byte) {
+//
+// With an importance vector (imp != null: the importance of each of the
+// half's 16 input channels) the error of a candidate is
+// sum_i wt_i * (x_i - xhat_i)^2 with wt_i = imp_i * sqrt(sigma^2 + x_i^2) and
+// sigma^2 the mean of x^2 over the half ("05 · Completed experiment"; the page
+// leaves sigma undefined).  The weights are computed once per half, every
+// step rounded once (fp64 sqrt is correctly rounded), in the same order as
+// the plain error, so the choice is reproducible bit for bit as well.
+__device__ void search_half(const float* x, const float* imp, uint32_t& code_word,
+                            uint32_t& byte) {
 #pragma clang fp contract(off)
   double xs[16];
   double amax = 0.0;
@@ -76,6 +85,15 @@ __device__ void search_half(const float* x, uint32_t& code_word, uint32_t& byte)
   for (int i = 0; i < 16; ++i) {
     xs[i] = (double)x[i];
     amax = fmax(amax, fabs(xs[i]));
+  }
+  double wt[16];
+  if (imp) {
+    double s2 = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s2 = s2 + xs[i] * xs[i];
+    const double sigma2 = s2 / 16.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wt[i] = (double)imp[i] * sqrt(sigma2 + xs[i] * xs[i]);
   }
   const double target = amax * 0.25;
   int start = 0;
@@ -95,7 +113,9 @@ __device__ void search_half(const float* x, uint32_t& code_word, uint32_t& byte)
       const double level = fabs(xs[i]) > lim ? 4.0 : 1.0;
       const double xh = (xs[i] < 0.0 ? -level : level) * s;
       const double e = xs[i] - xh;
-      sse = sse + e * e;
+      double t = e * e;
+      if (imp) t = wt[i] * t;
+      sse = sse + t;
     }
     const int rank = b < start ? 2 * (start - b) - 1 : 2 * (b - start);
     if (sse < best || (sse == best && rank < best_rank)) {
@@ -114,17 +134,21 @@ __device__ void search_half(const float* x, uint32_t& code_word, uint32_t& byte)
   byte = (uint32_t)best_b;
 }
 
+// imp: null, or the importance of each of the K input channels; block blk
+// covers columns 32*(blk % blocks_per_row) .. +31.
 __global__ __launch_bounds__(128) void quantize_weights_kernel(
-    const float* __restrict__ x, int64_t nblocks, uint16_t* __restrict__ w) {
+    const float* __restrict__ x, int64_t nblocks, int64_t blocks_per_row,
+    const float* __restrict__ imp, uint16_t* __restrict__ w) {
   for (int64_t blk = (int64_t)blockIdx.x * 128 + threadIdx.x; blk < nblocks;
        blk += (int64_t)gridDim.x * 128) {
   float v[32];
   const float* src = x + blk * 32;
 #pragma unroll
   for (int i = 0; i < 32; ++i) v[i] = src[i];
+  const float* ib = imp ? imp + (blk % blocks_per_row) * 32 : nullptr;
   uint32_t c0, c1, e0, e1;
-  search_half(v, c0, e0);
-  search_half(v + 16, c1, e1);
+  search_half(v, ib, c0, e0);
+  search_half(v + 16, ib ? ib + 16 : nullptr, c1, e1);
   uint16_t* dst = w + blk * 5;      // 10 bytes, 2-byte aligned
   dst[0] = (uint16_t)(c0 & 0xFFFFu);
   dst[1] = (uint16_t)(c0 >> 16);
@@ -135,11 +159,11 @@ __global__ __launch_bounds__(128) void quantize_weights_kernel(
 }
 
 hipError_t launch_quantize_weights(const float* x, int64_t N, int64_t K,
-                                   uint8_t* w, hipStream_t stream) {
+                                   const float* imp, uint8_t* w, hipStream_t stream) {
   const int64_t nblocks = N * (K / 32);
   const int64_t grid = std::min<int64_t>((nblocks + 127) / 128, kMaxGrid);
   hipLaunchKernelGGL(quantize_weights_kernel, dim3((uint32_t)grid), dim3(128),
-                     0, stream, x, nblocks, reinterpret_cast<uint16_t*>(w));
+                     0, stream, x, nblocks, K / 32, imp, reinterpret_cast<uint16_t*>(w));
   return hipGetLastError();
 }
 

@@ -55,7 +55,18 @@ rfp2_status rfp2_quantize_weights(const float* x, int64_t N, int64_t K,
     return RFP2_E_SHAPE;
   if (!aligned(x, 4) || !aligned(w, 2)) return RFP2_E_ALIGN;
   (void)hipGetLastError();
-  return from_hip(rfp2::launch_quantize_weights(x, N, K, w, stream));
+  return from_hip(rfp2::launch_quantize_weights(x, N, K, nullptr, w, stream));
+}
+
+rfp2_status rfp2_quantize_weights_imatrix(const float* x, int64_t N, int64_t K,
+                                          const float* importance, uint8_t* w,
+                                          hipStream_t stream) {
+  if (!x || !importance || !w) return RFP2_E_NULL;
+  if (N < 1 || N > kMaxRows || K < 32 || K % 32 != 0 || K > (int64_t(1) << 30))
+    return RFP2_E_SHAPE;
+  if (!aligned(x, 4) || !aligned(importance, 4) || !aligned(w, 2)) return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(rfp2::launch_quantize_weights(x, N, K, importance, w, stream));
 }
 
 rfp2_status rfp2_gemv(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,

@@ -14,7 +14,7 @@ constexpr int64_t kMaxGrid = 1 << 20;   // workgroups per launch (grid-stride be
 hipError_t launch_quantize_acts(const float* a, int64_t M, int64_t K, int8_t* q,
                                 float* d, hipStream_t stream);
 hipError_t launch_quantize_weights(const float* x, int64_t N, int64_t K,
-                                   uint8_t* w, hipStream_t stream);
+                                   const float* imp, uint8_t* w, hipStream_t stream);
 hipError_t launch_gemv(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
                        const float* d, int64_t M, float* y, hipStream_t stream);
 hipError_t launch_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,

@@ -95,6 +95,22 @@ rfp2_status rfp2_quantize_weights(const float* x, int64_t N, int64_t K,
                                   uint8_t* w, hipStream_t stream);
 
 /*
+ * rfp2_quantize_weights_imatrix -- rfp2_quantize_weights with the
+ * importance-weighted error of "05 · Completed experiment": a candidate
+ * scale's error is sum_i imp_i * sqrt(sigma^2 + x_i^2) * (x_i - xhat_i)^2
+ * over the half, where imp_i is the importance of the value's input channel
+ * and sigma^2 is the mean of x^2 over the half (the page leaves sigma
+ * undefined; this is the reading taken).  Weights and errors are fp64, one
+ * rounding per step, so the choice is reproducible.  The block layout,
+ * codebook and codes are unchanged; only which scale wins can differ.
+ *   importance [K] fp32, 4-byte aligned, finite and >= 0 (other values give
+ *   unspecified bytes).  x, w and the limits as rfp2_quantize_weights.
+ */
+rfp2_status rfp2_quantize_weights_imatrix(const float* x, int64_t N, int64_t K,
+                                          const float* importance, uint8_t* w,
+                                          hipStream_t stream);
+
+/*
  * rfp2_gemv -- y[m][n] = sum_k w[n][k] * q[m][k] * d[m][k/32] for a few
  * activation columns ("03 · Runtime": decode once, reuse for every column).
  *   w [N][K/32][10] bytes, 16-byte aligned.  q [M][K] int8, 16-byte aligned.

@@ -68,6 +68,19 @@ def routing(E: int, top_k: int, seed=ROUTE_SEED) -> np.ndarray:
     return np.random.default_rng(seed).choice(E, top_k, replace=False).astype(np.int32)
 
 
+IMP_SEED = 3
+
+
+def importance(K: int, seed=IMP_SEED, samples: int = 64) -> np.ndarray:
+    """fp32 [K] per-channel importance: the mean square, over `samples`
+    draws, of activations whose channels have log-normal gains (so channels
+    differ in importance, as calibration statistics E[a^2] do)."""
+    rng = np.random.default_rng(seed)
+    gain = np.exp(rng.normal(0.0, 0.5, K))
+    a = rng.standard_normal((samples, K)) * gain
+    return (a * a).mean(axis=0).astype(np.float32)
+
+
 def uniform_bytes(n: int, lo: int, hi: int, seed) -> np.ndarray:
     """uint8 [n] uniform in [lo, hi] (raw random bytes for edge-case tests)."""
     return np.random.default_rng(seed).integers(lo, hi + 1, n, dtype=np.int64).astype(np.uint8)

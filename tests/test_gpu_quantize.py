@@ -89,3 +89,45 @@ def test_quantize_weights_full_size_sampled_rows(name):
     packed = _gpu_quantize_weights(W)
     rows = sample_rows(N, 24, seed=11)
     assert np.array_equal(packed[rows], oracle.quantize_weights(W[rows]))
+
+
+def _gpu_quantize_weights_imatrix(W, imp):
+    N, K = W.shape
+    w = empty((N * K // 32 * 10,), torch.uint8)
+    rf.rfp2_quantize_weights_imatrix(to_dev(W), N, K, to_dev(imp), w)
+    return host(w).reshape(N, K // 32 * 10)
+
+
+def test_quantize_weights_imatrix_bitexact_full_small():
+    # the importance-weighted search ("05 · Completed experiment") on the GPU
+    # against the oracle, every block; it must differ from the plain search
+    announce("quantize_weights_imatrix 512x2048")
+    W = synth.weights(512, 2048, 0.02, seed=0)
+    imp = synth.importance(2048)
+    got = _gpu_quantize_weights_imatrix(W, imp)
+    assert np.array_equal(got, oracle.quantize_weights(W, imp))
+    assert not np.array_equal(got, oracle.quantize_weights(W))
+
+
+def test_quantize_weights_imatrix_special_importances():
+    announce("quantize_weights_imatrix special importances")
+    W = np.concatenate([synth.weights(8, 256, 0.02, seed=5),
+                        synth.weights(8, 256, 1.0, seed=6)])
+    K = W.shape[1]
+    one_hot = np.zeros(K, np.float32)
+    one_hot[::16] = 2.0                                  # one value per half
+    for imp in (np.zeros(K, np.float32), np.ones(K, np.float32), one_hot,
+                np.linspace(0, 4, K).astype(np.float32)):
+        assert np.array_equal(_gpu_quantize_weights_imatrix(W, imp),
+                              oracle.quantize_weights(W, imp))
+
+
+def test_quantize_weights_imatrix_full_size_sampled_rows():
+    announce("quantize_weights_imatrix 16384x5120")
+    cfg = synth.WORKLOADS["gemv_16384x5120"]
+    N, K = cfg["N"], cfg["K"]
+    W = synth.weights(N, K, cfg["sigma"], seed=cfg["wseed"])
+    imp = synth.importance(K)
+    packed = _gpu_quantize_weights_imatrix(W, imp)
+    rows = sample_rows(N, 24, seed=12)
+    assert np.array_equal(packed[rows], oracle.quantize_weights(W[rows], imp))
