@@ -36,6 +36,8 @@ _SIGNATURES = {
     "rfp2_gemm_f16": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
     "rfp2_moe_gemv": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p,
                        _c_p, _c_p], ctypes.c_int),
+    "rfp2_moe_gemv_tokens": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_i64, _c_p, _c_p,
+                              _c_p, _c_p, _c_p], ctypes.c_int),
     "rfp2_quant_gemv": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p], ctypes.c_int),
     "rfp2_quant_moe_gemv": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p,
                              _c_p, _c_p, _c_p], ctypes.c_int),
@@ -176,6 +178,17 @@ def rfp2_moe_gemv(w, E: int, N: int, K: int, ids, top_k: int, q, d, y, err=None,
         _ptr(ids, torch.int32, top_k, "ids"), top_k,
         _ptr(q, torch.int8, K, "q"), _ptr(d, torch.float32, _blocks(K), "d"),
         _ptr(y, torch.float32, top_k * N, "y"), errp, _stream(stream)))
+
+
+def rfp2_moe_gemv_tokens(w, E: int, N: int, K: int, ids, T: int, top_k: int, q, d, y,
+                         err=None, stream=None) -> None:
+    import torch
+    errp = None if err is None else _ptr(err, torch.int32, 1, "err")
+    _check("rfp2_moe_gemv_tokens", lib().rfp2_moe_gemv_tokens(
+        _ptr(w, torch.uint8, E * N * _blocks(K) * 10, "w"), E, N, K,
+        _ptr(ids, torch.int32, T * top_k, "ids"), T, top_k,
+        _ptr(q, torch.int8, T * K, "q"), _ptr(d, torch.float32, T * _blocks(K), "d"),
+        _ptr(y, torch.float32, T * top_k * N, "y"), errp, _stream(stream)))
 
 
 def rfp2_quant_gemv(w, N: int, K: int, a, q, d, y, stream=None) -> None:

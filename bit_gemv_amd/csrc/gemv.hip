@@ -47,6 +47,7 @@ namespace rfp2 {
 
 namespace gemv_detail {
 GemvFn pick_m1(int jt);
+GemvFn pick_moe_tokens(int T);   // gemv_moe.hip
 GemvFn pick_m2(int jt);
 GemvFn pick_m3(int jt);
 GemvFn pick_m4(int jt);
@@ -152,7 +153,7 @@ hipError_t launch_gemv(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
   for (int64_t m0 = 0; m0 < M; m0 += cols) {
     const int mc = (int)std::min<int64_t>(cols, M - m0);
     Params p{w, (int)N, (int)K, q + m0 * K, d + m0 * (K / 32), y + m0 * N,
-             g.lshift, g.wk, g.J, nullptr, 0, nullptr, nullptr, nullptr, nullptr};
+             g.lshift, g.wk, g.J, nullptr, 0, nullptr, 1, 0, nullptr, nullptr, nullptr};
     hipLaunchKernelGGL(pick_kernel(mc, g.jt), grid, dim3(64 * g.wk), lds_bytes(mc, g),
                        stream, p);
     const hipError_t e = hipGetLastError();
@@ -168,9 +169,27 @@ hipError_t launch_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
   const Geometry g = geometry(K, 1, N * top_k);
   const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows), (uint32_t)top_k);
   Params p{w, (int)N, (int)K, q, d, y, g.lshift, g.wk, g.J, ids, (int)E, err,
-           nullptr, nullptr, nullptr};
+           (int)top_k, (int)top_k, nullptr, nullptr, nullptr};
   const GemvFn fn = pick<1, true>(g.jt);
   hipLaunchKernelGGL(fn, grid, dim3(64 * g.wk), lds_bytes(1, g), stream, p);
+  return hipGetLastError();
+}
+
+// Several tokens, each routed to top_k experts: slot s = t * top_k + j.  The
+// slots routed to one expert are computed together (one decode of the
+// expert's rows for up to T tokens); the one-column split is used (the
+// expert matrices are small and the groups are scattered over experts).
+hipError_t launch_moe_gemv_tokens(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                                  const int32_t* ids, int64_t T, int64_t top_k,
+                                  const int8_t* q, const float* d, float* y, int32_t* err,
+                                  hipStream_t stream) {
+  if (T == 1) return launch_moe_gemv(w, E, N, K, ids, top_k, q, d, y, err, stream);
+  const Geometry g = geometry(K, 1, N * T * top_k);
+  const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows), (uint32_t)(T * top_k));
+  Params p{w, (int)N, (int)K, q, d, y, g.lshift, g.wk, g.J, ids, (int)E, err, (int)top_k,
+           (int)(T * top_k), nullptr, nullptr, nullptr};
+  hipLaunchKernelGGL(gemv_detail::pick_moe_tokens((int)T), grid, dim3(64 * g.wk), lds_bytes((int)T, g),
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -189,7 +208,8 @@ hipError_t launch_quant_gemv(const uint8_t* w, int64_t N, int64_t K, const float
     return launch_gemv(w, N, K, q, d, 1, y, stream);
   }
   const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows));
-  Params p{w, (int)N, (int)K, q, d, y, g.lshift, g.wk, g.J, nullptr, 0, nullptr, a, q, d};
+  Params p{w, (int)N, (int)K, q, d, y, g.lshift, g.wk, g.J, nullptr, 0, nullptr, 1, 0,
+           a, q, d};
   hipLaunchKernelGGL((gemv_kernel<1, 1, false, true>), grid, dim3(64 * g.wk), lds_bytes(1, g),
                      stream, p);
   return hipGetLastError();
@@ -206,7 +226,8 @@ hipError_t launch_quant_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t
     return launch_moe_gemv(w, E, N, K, ids, top_k, q, d, y, err, stream);
   }
   const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows), (uint32_t)top_k);
-  Params p{w, (int)N, (int)K, q, d, y, g.lshift, g.wk, g.J, ids, (int)E, err, a, q, d};
+  Params p{w, (int)N, (int)K, q, d, y, g.lshift, g.wk, g.J, ids, (int)E, err, (int)top_k,
+           (int)top_k, a, q, d};
   hipLaunchKernelGGL((gemv_kernel<1, 1, true, true>), grid, dim3(64 * g.wk), lds_bytes(1, g),
                      stream, p);
   return hipGetLastError();

@@ -24,9 +24,11 @@ struct Params {
   int lshift;      // log2(lanes that share a row inside one wave)
   int wk;          // waves per workgroup: the row's groups are split among them
   int J;           // groups per lane
-  const int32_t* ids;   // routed experts (MoE form) or null
+  const int32_t* ids;   // routed experts (MoE form) or null: one per slot
   int E;
   int32_t* err;
+  int top_k;            // MoE form: slots per token (slot s belongs to token s / top_k)
+  int S;                // MoE form: number of slots
   const float* a;       // fp32 activations (quantizing form) or null
   int8_t* qo;           // quantizing form: q and d written by workgroup 0
   float* dout;
@@ -41,7 +43,7 @@ __device__ __forceinline__ void group_product(const uint32_t (&dw)[20],
                                               const uint32_t* act, int act_stride,
                                               const float* dact, int d_stride,
                                               float (&acc)[M], uint32_t& bad_lo,
-                                              uint32_t& bad_hi) {
+                                              uint32_t& bad_hi, int ncols = M) {
 #pragma unroll
   for (int jb = 0; jb < 8; ++jb) {
     // block jb occupies bytes 10*jb .. 10*jb+9 of the group
@@ -70,6 +72,7 @@ __device__ __forceinline__ void group_product(const uint32_t (&dw)[20],
       bad_hi |= sc;
 #pragma unroll
     for (int m = 0; m < M; ++m) {
+      if (m >= ncols) break;                  // (uniform) unused columns of a group
       const uint32_t* a = act + m * act_stride + jb * 8;
       const uint4 A0 = *reinterpret_cast<const uint4*>(a);
       const uint4 A1 = *reinterpret_cast<const uint4*>(a + 4);
@@ -295,13 +298,46 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
   const int row_bytes = (K >> 8) * 80;
 
   const uint8_t* wb = p.w;
-  float* yb = p.y;
   bool id_ok = true;
+  // Column m of this workgroup reads token col_tok[m] and writes y row
+  // col_out[m].  Dense form: column m is token m.  MoE form: blockIdx.y is
+  // a slot; with M > 1 (several tokens) the slots routed to the same expert
+  // are grouped, so the expert's rows are decoded once for all of them: the
+  // workgroup of the first slot of every run of M same-expert slots (in slot
+  // order) computes that run, the others exit at once.  Unused columns of a
+  // shorter run are skipped.
+  int ncols = M;
+  int col_tok[M], col_out[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) col_tok[m] = col_out[m] = m;
   if (MOE) {
-    const int e = p.ids[blockIdx.y];
+    const int s0 = blockIdx.y;
+    const int e = p.ids[s0];
+    col_tok[0] = s0 / p.top_k;
+    col_out[0] = s0;
+    if (M > 1) {
+      // one ballot covers the slots (S <= 64): which of them use expert e
+      const int v = lane < p.S ? p.ids[lane] : ~e;
+      uint64_t mask = __ballot(v == e);
+      const uint64_t below = (uint64_t(1) << s0) - 1;
+      if (__popcll(mask & below) % M) return;   // uniform: the whole workgroup
+      mask &= ~below;
+      ncols = min(__popcll(mask), M);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        if (m < ncols) {
+          const int u = __ffsll((long long)mask) - 1;
+          col_out[m] = u;
+          col_tok[m] = u / p.top_k;
+          mask &= mask - 1;
+        } else {
+          col_out[m] = col_out[m - 1];
+          col_tok[m] = col_tok[m - 1];
+        }
+      }
+    }
     id_ok = e >= 0 && e < p.E;
     wb = p.w + (int64_t)(id_ok ? e : 0) * (int64_t)N * row_bytes;
-    yb = p.y + (int64_t)blockIdx.y * N;
   }
   wb += (int64_t)row0 * row_bytes;
 
@@ -321,6 +357,13 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
   auto group_of = [&](int lgl) {
     return (((lgl >> ls) * p.wk + wave) << ls) + (lgl & (L - 1));
   };
+  // token of a lane-dependent column index: lane c of tok_lanes holds
+  // col_tok[c], read back with a lane shuffle (no indexed register array,
+  // which the compiler would place in scratch memory)
+  int tok_lanes = col_tok[0];
+#pragma unroll
+  for (int c = 1; c < M; ++c) tok_lanes = lane == c ? col_tok[c] : tok_lanes;
+  auto token_of = [&](int m) { return M == 1 ? col_tok[0] : __shfl(tok_lanes, m, 64); };
 
   // The weight offsets are pure arithmetic: done first, they are ready when
   // the loads go out.
@@ -370,7 +413,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
         if (piece < 16 && g < M * ag) {
           const int m = M == 1 ? 0 : g / ag;
           const int lgl = g - m * ag;
-          off = (uint32_t)(m * K + (group_of(lgl) * 16 + piece) * 16);
+          off = (uint32_t)(token_of(m) * K + (group_of(lgl) * 16 + piece) * 16);
         }
         dma16(p.q, off, m0 + 1024 * r);
       }
@@ -380,7 +423,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
         const int g = i >> 3;
         const int m = M == 1 ? 0 : g / ag;
         const int lgl = g - m * ag;
-        dma4(p.d, (uint32_t)(4 * (m * nb + group_of(lgl) * 8 + (i & 7))), m0d + 256 * r);
+        dma4(p.d, (uint32_t)(4 * (token_of(m) * nb + group_of(lgl) * 8 + (i & 7))),
+             m0d + 256 * r);
       }
     }
 #pragma unroll
@@ -427,7 +471,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
                  ring_m0 + 5120 * buf_i);
     const int lgl = (j << ls) + t;
     group_product<M>(buf, alds + lgl * kGroupDwords, act_stride, dlds + lgl * 8, ag * 8, acc,
-                     bad_lo, bad_hi);
+                     bad_lo, bad_hi, ncols);
   }
 
   // row sum: xor shuffles over the L lanes of the row, then over the waves
@@ -458,7 +502,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
     const float fix = scale_fix();
 #pragma unroll
     for (int m = 0; m < M; ++m)
-      yb[(int64_t)m * N + row] = id_ok ? acc[m] * fix : __builtin_nanf("");
+      if (m < ncols)
+        p.y[(int64_t)col_out[m] * N + row] = id_ok ? acc[m] * fix : __builtin_nanf("");
   }
   if (MOE && !id_ok && blockIdx.x == 0 && threadIdx.x == 0 && p.err != nullptr)
     p.err[0] = 1;

@@ -123,6 +123,22 @@ rfp2_status rfp2_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
   return from_hip(rfp2::launch_moe_gemv(w, E, N, K, ids, top_k, q, d, y, err, stream));
 }
 
+rfp2_status rfp2_moe_gemv_tokens(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                                 const int32_t* ids, int64_t T, int64_t top_k,
+                                 const int8_t* q, const float* d, float* y, int32_t* err,
+                                 hipStream_t stream) {
+  if (!w || !ids || !q || !d || !y) return RFP2_E_NULL;
+  if (E < 1 || E > kMaxRows || N < 1 || N > kMaxRows || T < 1 || T > RFP2_GEMV_MAX_M ||
+      top_k < 1 || T * top_k > 64 || !product_k_ok(K))
+    return RFP2_E_SHAPE;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(d, 4) || !aligned(y, 4) ||
+      !aligned(ids, 4) || (err && !aligned(err, 4)))
+    return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(
+      rfp2::launch_moe_gemv_tokens(w, E, N, K, ids, T, top_k, q, d, y, err, stream));
+}
+
 rfp2_status rfp2_quant_gemv(const uint8_t* w, int64_t N, int64_t K, const float* a,
                             int8_t* q, float* d, float* y, hipStream_t stream) {
   if (!w || !a || !q || !d || !y) return RFP2_E_NULL;

@@ -21,6 +21,10 @@ hipError_t launch_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
                            const int32_t* ids, int64_t top_k, const int8_t* q,
                            const float* d, float* y, int32_t* err,
                            hipStream_t stream);
+hipError_t launch_moe_gemv_tokens(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                                  const int32_t* ids, int64_t T, int64_t top_k,
+                                  const int8_t* q, const float* d, float* y, int32_t* err,
+                                  hipStream_t stream);
 hipError_t launch_quant_gemv(const uint8_t* w, int64_t N, int64_t K, const float* a,
                              int8_t* q, float* d, float* y, hipStream_t stream);
 hipError_t launch_quant_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,

@@ -166,6 +166,29 @@ rfp2_status rfp2_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
                           float* y, int32_t* err, hipStream_t stream);
 
 /*
+ * rfp2_moe_gemv_tokens -- routed-expert GEMV for T tokens at once (e.g. the
+ * tokens of a speculative-decoding verification batch).  Slot s = t * top_k
+ * + j of token t is routed to expert ids[s]; the slots routed to one expert
+ * are computed together, so each expert's rows are expanded once and reused
+ * for every token routed to it ("Why AMD-friendly does not mean always
+ * faster": expand a block once, reuse it across all activation columns).
+ *   w    E experts back to back, each [N][K/32][10] bytes; 16-byte aligned.
+ *   ids  [T][top_k] int32 on the device.
+ *   q, d [T][K] int8 (16-byte aligned) and [T][K/32] fp32.
+ *   y    [T][top_k][N] fp32: row s = expert ids[s] applied to token s / top_k.
+ *   err  as rfp2_moe_gemv (an id outside [0, E) gives a NaN row and *err = 1).
+ * Duplicate ids are legal.  T = 1 is rfp2_moe_gemv.  Each row of y is within
+ * the fp32 bound of the product, but the order of its additions may differ
+ * from rfp2_moe_gemv's for the same token.
+ * Requires E >= 1, N >= 1, 1 <= T <= RFP2_GEMV_MAX_M, top_k >= 1,
+ * T * top_k <= 64, 256 <= K <= 32768, K % 256 == 0.
+ */
+rfp2_status rfp2_moe_gemv_tokens(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                                 const int32_t* ids, int64_t T, int64_t top_k,
+                                 const int8_t* q, const float* d, float* y, int32_t* err,
+                                 hipStream_t stream);
+
+/*
  * rfp2_quant_gemv -- one token end to end: quantizes the fp32 activations a
  * exactly as rfp2_quantize_acts does, writing q and d, and computes
  * y = W * a as rfp2_gemv does from that q and d ("03 · Runtime": the int8

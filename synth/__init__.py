@@ -81,6 +81,21 @@ def importance(K: int, seed=IMP_SEED, samples: int = 64) -> np.ndarray:
     return (a * a).mean(axis=0).astype(np.float32)
 
 
+def routing_tokens(E: int, top_k: int, T: int, share: float, seed=ROUTE_SEED) -> np.ndarray:
+    """int32 [T, top_k] expert ids for T consecutive tokens.  Token 0 draws
+    top_k distinct experts uniformly; each later token keeps each expert of
+    the token before it with probability `share` and fills the rest with
+    fresh distinct draws (share 0: independent tokens, 1: identical routing)."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((T, top_k), np.int32)
+    out[0] = rng.choice(E, top_k, replace=False)
+    for t in range(1, T):
+        keep = [e for e in out[t - 1] if rng.random() < share]
+        rest = [e for e in rng.permutation(E) if e not in keep][:top_k - len(keep)]
+        out[t] = np.array(keep + rest, np.int32)
+    return out
+
+
 def uniform_bytes(n: int, lo: int, hi: int, seed) -> np.ndarray:
     """uint8 [n] uniform in [lo, hi] (raw random bytes for edge-case tests)."""
     return np.random.default_rng(seed).integers(lo, hi + 1, n, dtype=np.int64).astype(np.uint8)
