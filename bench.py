@@ -39,8 +39,9 @@ COLD_BYTES = 1 << 30           # distinct weight bytes rotated through
 # The large-layer GEMV is the workload on which an HBM fraction is meaningful
 # (25 MiB of weights; the 5 MiB projection is latency-bound on this GPU).
 DEFAULT_WORKLOAD = "gemv_16384x5120"
-SECONDARY = ["gemv_4096x4096", "gemm_512x14336x4096", "gemm_f16_512x14336x4096"]
-KERNEL_SOURCES = ["rfp2_device.h", "gemv_kernel.h", "gemv.hip", "gemm.hip",
+SECONDARY = ["gemv_4096x4096", "moe_128x1536x4096_top8_t4", "gemm_512x14336x4096",
+             "gemm_f16_512x14336x4096"]
+KERNEL_SOURCES = ["rfp2_device.h", "gemv_kernel.h", "gemv.hip", "gemv_moe.hip", "gemm.hip",
                   "gemm_f16.hip", "quantize.hip"]
 
 
@@ -69,6 +70,13 @@ def algorithmic(cfg, one_launch: bool = False) -> dict:
         tk = cfg["top_k"]
         weights_y = tk * N * w_row + 4 * tk + 4 * tk * N
         ops = 2 * tk * N * K
+    elif cfg["op"] == "moe_tokens":
+        # every distinct routed expert once, ids, and one y row per slot
+        import synth
+        ids = synth.routing_tokens(cfg["E"], cfg["top_k"], M, cfg["share"])
+        slots = M * cfg["top_k"]
+        weights_y = len(set(ids.reshape(-1).tolist())) * N * w_row + 4 * slots + 4 * slots * N
+        ops = 2 * slots * N * K
     else:
         weights_y = N * w_row + 4 * M * N
         ops = 2 * M * N * K
@@ -184,7 +192,8 @@ def measure_quantizer(workload: str, reps: int = 5) -> dict:
     return out
 
 
-def measure(workload: str, steps: int, warmup: int, two_launch: bool = False) -> dict:
+def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
+            per_token: bool = False) -> dict:
     """Time one workload on cuda:0; returns the fields of its bench line."""
     import torch
     import bit_gemv_amd as rf
@@ -200,7 +209,7 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False) ->
 
     with torch.cuda.stream(stream):
         # ---- weights, quantized on the GPU, then copied until >= 1 GiB
-        if cfg["op"] == "moe":
+        if cfg["op"] in ("moe", "moe_tokens"):
             E, top_k = cfg["E"], cfg["top_k"]
             per_copy = E * N * w_row
             master = torch.empty(per_copy, dtype=torch.uint8, device=dev)
@@ -208,7 +217,11 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False) ->
                 We = torch.from_numpy(synth.expert_weights(e, N, K, cfg["sigma"],
                                                            seed=cfg["wseed"])).to(dev)
                 rf.rfp2_quantize_weights(We, N, K, master[e * N * w_row:(e + 1) * N * w_row])
-            ids = torch.from_numpy(synth.routing(E, top_k)).to(dev)
+            if cfg["op"] == "moe":
+                ids = torch.from_numpy(synth.routing(E, top_k)).to(dev)
+            else:
+                ids = torch.from_numpy(
+                    synth.routing_tokens(E, top_k, M, cfg["share"]).reshape(-1)).to(dev)
         else:
             per_copy = N * w_row
             master = torch.empty(per_copy, dtype=torch.uint8, device=dev)
@@ -220,7 +233,8 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False) ->
         a = torch.from_numpy(synth.activations(M, K)).to(dev)
         q = torch.empty((M, K), dtype=torch.int8, device=dev)
         d = torch.empty((M, K // 32), dtype=torch.float32, device=dev)
-        rows_out = cfg["top_k"] if cfg["op"] == "moe" else M
+        rows_out = {"moe": cfg.get("top_k"), "moe_tokens": M * cfg.get("top_k", 1)}.get(
+            cfg["op"], M)
         y = torch.empty((rows_out, N), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
 
@@ -233,6 +247,14 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False) ->
                 rf.rfp2_quant_gemv(w, N, K, a, q, d, y, st)
             elif cfg["op"] == "moe":
                 rf.rfp2_moe_gemv(w, cfg["E"], N, K, ids, cfg["top_k"], q, d, y, None, st)
+            elif cfg["op"] == "moe_tokens" and per_token:
+                tk = cfg["top_k"]
+                for t in range(M):   # one single-token call per token
+                    rf.rfp2_moe_gemv(w, cfg["E"], N, K, ids[t * tk:(t + 1) * tk], tk, q[t],
+                                     d[t], y[t * tk:(t + 1) * tk], None, st)
+            elif cfg["op"] == "moe_tokens":
+                rf.rfp2_moe_gemv_tokens(w, cfg["E"], N, K, ids, M, cfg["top_k"], q, d, y,
+                                        None, st)
             elif cfg["op"] == "gemm":
                 rf.rfp2_gemm(w, N, K, q, d, M, y, st)
             elif cfg["op"] == "gemm_f16":
@@ -303,8 +325,9 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False) ->
     torch.cuda.empty_cache()
 
     khash = kernel_hash()
-    kernel = {"moe": "rfp2_moe_gemv", "gemm": "rfp2_gemm",
-              "gemm_f16": "rfp2_gemm_f16"}.get(cfg["op"], "rfp2_gemv")
+    kernel = {"moe": "rfp2_moe_gemv", "gemm": "rfp2_gemm", "gemm_f16": "rfp2_gemm_f16",
+              "moe_tokens": f"{M} x rfp2_moe_gemv" if per_token else "rfp2_moe_gemv_tokens",
+              }.get(cfg["op"], "rfp2_gemv")
     if one:
         kernel = "rfp2_quant_moe_gemv" if cfg["op"] == "moe" else "rfp2_quant_gemv"
     if cfg["op"] in ("gemm", "gemm_f16"):
@@ -325,8 +348,10 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False) ->
                 kernel_us=kern_ms * 1e3, algorithmic_bytes=alg["product_bytes"],
                 algorithmic_ops=alg["ops"])
     config = {"workload": workload, "M": M, "N": N, "K": K}
-    if cfg["op"] == "moe":
+    if cfg["op"] in ("moe", "moe_tokens"):
         config.update(experts=cfg["E"], top_k=cfg["top_k"])
+    if cfg["op"] == "moe_tokens":
+        config.update(tokens=M, expert_share=cfg["share"])
     config.update(weight_copies=copies, weight_bytes_per_copy=per_copy,
                   step=kernel if one else "rfp2_quantize_acts + " + kernel,
                   graph_steps=per_graph,
@@ -344,6 +369,8 @@ def main(argv=None) -> int:
     ap.add_argument("--secondary", default=",".join(SECONDARY),
                     help="comma-separated workloads also measured (empty: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--per-token", action="store_true",
+                    help="multi-token MoE workloads as one single-token call per token")
     ap.add_argument("--quantizer", action="store_true",
                     help="also time the weight quantizers (plain and importance-weighted)")
     ap.add_argument("--two-launch", action="store_true",
@@ -356,7 +383,7 @@ def main(argv=None) -> int:
               file=sys.stderr)
         return 2
 
-    r = measure(args.workload, args.steps, args.warmup, args.two_launch)
+    r = measure(args.workload, args.steps, args.warmup, args.two_launch, args.per_token)
     out = {
         "metric": r["metric"], "value": r["value"], "unit": r["unit"], "n_gpus": 1,
         "steps": r["steps"], "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
@@ -366,7 +393,7 @@ def main(argv=None) -> int:
     }
     secondary = []
     for wl in [w for w in args.secondary.split(",") if w and w != args.workload]:
-        s = measure(wl, args.steps, args.warmup, args.two_launch)
+        s = measure(wl, args.steps, args.warmup, args.two_launch, args.per_token)
         secondary.append({"workload": wl, "metric": s["metric"], "value": s["value"],
                           "unit": s["unit"], "ms_per_step": s["ms_per_step"],
                           "roofline": {k: s["roofline"][k] for k in

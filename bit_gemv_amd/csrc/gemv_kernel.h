@@ -12,7 +12,8 @@ namespace gemv_detail {
 // L lanes of a row, which read L consecutive groups, hit different banks.
 constexpr int kGroupPieces = 17;
 constexpr int kGroupDwords = 4 * kGroupPieces;
-constexpr int kMaxLdsBytes = 65536;  // LDS budget per workgroup
+constexpr int kMaxLdsBytes = 65536;  // LDS budget per workgroup (dense GEMV)
+constexpr int kMaxLdsBytesPerBlock = 163840;  // gfx950: 160 KiB per workgroup
 constexpr int kMaxWaves = 8;         // waves per workgroup (each owns a K slice)
 
 struct Params {
@@ -350,6 +351,12 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
   const int act_rounds = (n_pieces + 63) >> 6;
   const int d_rounds = (n_scales + 63) >> 6;
   const int wave_dwords = JT * 1280 + act_rounds * 256 + d_rounds * 64;
+  // what this workgroup actually loads and transposes (a short MoE group
+  // stages only its own columns; the LDS carving above is for M)
+  const int use_pieces = ncols * ag * kGroupPieces;
+  const int use_scales = ncols * ag * 8;
+  const int use_act_rounds = (use_pieces + 63) >> 6;
+  const int use_d_rounds = (use_scales + 63) >> 6;
   uint32_t* wlds = lds + wave * wave_dwords;
   uint32_t* alds = wlds + JT * 1280;
   float* dlds = reinterpret_cast<float*>(alds + act_rounds * 256);
@@ -406,20 +413,23 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
     // rounding slack re-read the first piece.
     {
       const uint32_t m0 = lds_m0(alds);
-      for (int r = 0; r < act_rounds; ++r) {
+      for (int r = 0; r < use_act_rounds; ++r) {
         const int pc = 64 * r + lane;
         const int g = pc / kGroupPieces, piece = pc - g * kGroupPieces;
-        uint32_t off = 0;
-        if (piece < 16 && g < M * ag) {
-          const int m = M == 1 ? 0 : g / ag;
-          const int lgl = g - m * ag;
-          off = (uint32_t)(token_of(m) * K + (group_of(lgl) * 16 + piece) * 16);
-        }
+        const bool used = piece < 16 && g < ncols * ag;
+        const int gu = used ? g : 0;
+        const int m = M == 1 ? 0 : gu / ag;
+        const int lgl = gu - m * ag;
+        // the token lookup is a lane shuffle: every lane must take part (a
+        // lane left out of it reads as 0 to the others)
+        const int tok = token_of(m);
+        const uint32_t off =
+            used ? (uint32_t)(tok * K + (group_of(lgl) * 16 + piece) * 16) : 0u;
         dma16(p.q, off, m0 + 1024 * r);
       }
       const uint32_t m0d = lds_m0(dlds);
-      for (int r = 0; r < d_rounds; ++r) {
-        const int i = min(64 * r + lane, n_scales - 1);
+      for (int r = 0; r < use_d_rounds; ++r) {
+        const int i = min(64 * r + lane, use_scales - 1);
         const int g = i >> 3;
         const int m = M == 1 ? 0 : g / ag;
         const int lgl = g - m * ag;
@@ -434,7 +444,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
 
     // transpose each half's 16 activations in place into the lane order of
     // the expanded weights
-    for (int pc = lane; pc < n_pieces; pc += 64) {
+    for (int pc = lane; pc < use_pieces; pc += 64) {
       if (pc % kGroupPieces == 16) continue;
       uint4* a = reinterpret_cast<uint4*>(alds) + pc;
       const uint4 x = *a;

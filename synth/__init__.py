@@ -22,6 +22,11 @@ WORKLOADS = {
     # routed experts: 128 up-projections 1536x4096, one token, top-8
     "moe_128x1536x4096_top8": dict(op="moe", M=1, E=128, top_k=8, N=1536,
                                    K=4096, sigma=0.02, wseed=0),
+    # the same bank for 4 consecutive tokens (e.g. a speculative-decoding
+    # verification batch), half of each token's experts kept from the token
+    # before: tokens grouped per expert, each expert decoded once
+    "moe_128x1536x4096_top8_t4": dict(op="moe_tokens", M=4, E=128, top_k=8, N=1536,
+                                      K=4096, sigma=0.02, wseed=0, share=0.5),
     # large layer GEMV (25.0 MiB of ROCmFP2 weights) at 1 and 4 tokens
     "gemv_16384x5120": dict(op="gemv", M=1, N=16384, K=5120, sigma=0.015,
                             wseed=0),

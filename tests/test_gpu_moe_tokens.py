@@ -25,15 +25,17 @@ def run_tokens(bank, E, N, K, ids, q, d):
 
 def check_rows(y, bank, E, N, K, ids, q, d):
     T, top_k = ids.shape
+    refs = {}                   # expert -> (oracle products, |w a| sums) for every token
     for t in range(T):
         for j in range(top_k):
             s, e = t * top_k + j, int(ids[t, j])
             if not 0 <= e < E:
                 assert np.isnan(y[s]).all(), f"slot {s}: bad id {e} not NaN"
                 continue
-            assert_within_bound(y[s], oracle.ref_gemv(bank[e], N, K, q[t:t + 1], d[t:t + 1])[0],
-                                oracle.abs_product_sums(bank[e], N, K, q[t:t + 1],
-                                                        d[t:t + 1])[0],
+            if e not in refs:
+                refs[e] = (oracle.ref_gemv(bank[e], N, K, q, d),
+                           oracle.abs_product_sums(bank[e], N, K, q, d))
+            assert_within_bound(y[s], refs[e][0][t], refs[e][1][t],
                                 f"token {t} slot {j} expert {e}")
 
 
@@ -52,8 +54,12 @@ def make_ids(kind, E, T, top_k, rng):
     return ids
 
 
+# (8, 8, 4096): four groups per lane, 70 KB of LDS; (8, 4, 8192): 100 KB, the
+# direct loads land above 64 KB; (8, 2, 16384): 7 tokens then 1 (the one-token
+# kernel); (5, 2, 32768): chunks of 3 and 2 tokens
 @pytest.mark.parametrize("T,top_k,K", [(2, 3, 1024), (3, 8, 2048), (4, 8, 4096),
-                                       (8, 8, 1024), (5, 1, 512)])
+                                       (8, 8, 1024), (5, 1, 512), (8, 8, 4096),
+                                       (8, 4, 8192), (8, 2, 16384), (5, 2, 32768)])
 @pytest.mark.parametrize("kind", ["independent", "shared", "duplicates", "one_expert", "bad"])
 def test_moe_tokens_against_oracle(T, top_k, K, kind):
     announce("moe_tokens", T, top_k, K, kind)
