@@ -25,6 +25,6 @@ from .rfp2 import (  # noqa: F401
     pack_block, unpack_block, pack_matrix, unpack_matrix,
     start_byte, quantize_half, quantize_weights, dequantize_weights,
     quantize_acts, dequantize_acts, decoded_int8, half_sums,
-    ref_gemv, ref_gemm, ref_moe_gemv, abs_product_sums,
+    ref_gemv, ref_gemm, ref_moe_gemv, ref_moe_batch, sort_by_expert, abs_product_sums,
     row_bytes, matrix_bytes,
 )

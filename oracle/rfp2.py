@@ -391,3 +391,46 @@ def ref_moe_gemv(bank: np.ndarray, E: int, N: int, K: int, ids, q: np.ndarray,
         if 0 <= e < E:
             y[j] = ref_gemv(bank[e], N, K, q, d)[0]
     return y
+
+
+def sort_by_expert(ids, E: int):
+    """Routed slots grouped by expert: the token order of a batched expert
+    product ("04 · Measured evidence" / "07 · Recipe decision": prompt
+    batches through the routed experts, where prefill dominates).
+
+    ids: the expert of each slot, slot s = t*top_k + j for token t's j-th
+    expert.  Every slot whose id lies in [0, E) is put in the bucket of its
+    expert, buckets in expert order, slots inside a bucket in increasing slot
+    order; slots with another id are left out.
+    -> (offsets int64 [E+1], order int64 [offsets[E]]): expert e's slots are
+    order[offsets[e]:offsets[e+1]].
+    """
+    ids = [int(i) for i in np.asarray(ids).reshape(-1)]
+    buckets = [[] for _ in range(E)]
+    for s, e in enumerate(ids):
+        if 0 <= e < E:
+            buckets[e].append(s)
+    offsets = [0]
+    for b in buckets:
+        offsets.append(offsets[-1] + len(b))
+    order = [s for b in buckets for s in b]
+    return np.array(offsets, dtype=np.int64), np.array(order, dtype=np.int64)
+
+
+def ref_moe_batch(bank: np.ndarray, E: int, N: int, K: int, ids, q: np.ndarray,
+                  d: np.ndarray) -> np.ndarray:
+    """Routed-expert products for T tokens (a prompt batch).
+
+    ids: [T, top_k]; q, d: the T tokens' int8 activations and scales.  Row
+    t*top_k + j of the result is expert ids[t, j] applied to token t (NaN for
+    an id outside [0, E)): the one-token product of each token, stacked.
+    -> fp64 [T*top_k, N].
+    """
+    T = q.shape[0]
+    ids = np.asarray(ids).reshape(T, -1)
+    top_k = ids.shape[1]
+    y = np.empty((T * top_k, N))
+    for t in range(T):
+        y[t * top_k:(t + 1) * top_k] = ref_moe_gemv(bank, E, N, K, ids[t], q[t:t + 1],
+                                                    d[t:t + 1])
+    return y
