@@ -40,9 +40,9 @@ COLD_BYTES = 1 << 30           # distinct weight bytes rotated through
 # (25 MiB of weights; the 5 MiB projection is latency-bound on this GPU).
 DEFAULT_WORKLOAD = "gemv_16384x5120"
 SECONDARY = ["gemv_4096x4096", "moe_128x1536x4096_top8_t4", "gemm_512x14336x4096",
-             "gemm_f16_512x14336x4096"]
+             "gemm_f16_512x14336x4096", "moe_gemm_128x1536x4096_top8_t512"]
 KERNEL_SOURCES = ["rfp2_device.h", "gemv_kernel.h", "gemv.hip", "gemv_moe.hip", "gemm.hip",
-                  "gemm_f16.hip", "quantize.hip"]
+                  "gemm_f16.hip", "moe_sort.hip", "quantize.hip"]
 
 
 def kernel_hash() -> str:
@@ -70,7 +70,7 @@ def algorithmic(cfg, one_launch: bool = False) -> dict:
         tk = cfg["top_k"]
         weights_y = tk * N * w_row + 4 * tk + 4 * tk * N
         ops = 2 * tk * N * K
-    elif cfg["op"] == "moe_tokens":
+    elif cfg["op"] in ("moe_tokens", "moe_gemm"):
         # every distinct routed expert once, ids, and one y row per slot
         import synth
         ids = synth.routing_tokens(cfg["E"], cfg["top_k"], M, cfg["share"])
@@ -209,7 +209,7 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
 
     with torch.cuda.stream(stream):
         # ---- weights, quantized on the GPU, then copied until >= 1 GiB
-        if cfg["op"] in ("moe", "moe_tokens"):
+        if cfg["op"] in ("moe", "moe_tokens", "moe_gemm"):
             E, top_k = cfg["E"], cfg["top_k"]
             per_copy = E * N * w_row
             master = torch.empty(per_copy, dtype=torch.uint8, device=dev)
@@ -233,8 +233,12 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
         a = torch.from_numpy(synth.activations(M, K)).to(dev)
         q = torch.empty((M, K), dtype=torch.int8, device=dev)
         d = torch.empty((M, K // 32), dtype=torch.float32, device=dev)
-        rows_out = {"moe": cfg.get("top_k"), "moe_tokens": M * cfg.get("top_k", 1)}.get(
-            cfg["op"], M)
+        rows_out = {"moe": cfg.get("top_k"), "moe_tokens": M * cfg.get("top_k", 1),
+                    "moe_gemm": M * cfg.get("top_k", 1)}.get(cfg["op"], M)
+        ws = None
+        if cfg["op"] == "moe_gemm":
+            ws = torch.empty(rf.rfp2_moe_gemm_workspace_bytes(cfg["E"], M, cfg["top_k"]),
+                             dtype=torch.uint8, device=dev)
         y = torch.empty((rows_out, N), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
 
@@ -255,6 +259,9 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
             elif cfg["op"] == "moe_tokens":
                 rf.rfp2_moe_gemv_tokens(w, cfg["E"], N, K, ids, M, cfg["top_k"], q, d, y,
                                         None, st)
+            elif cfg["op"] == "moe_gemm":
+                rf.rfp2_moe_gemm(w, cfg["E"], N, K, ids, M, cfg["top_k"], q, d, y, None, ws,
+                                 st)
             elif cfg["op"] == "gemm":
                 rf.rfp2_gemm(w, N, K, q, d, M, y, st)
             elif cfg["op"] == "gemm_f16":
@@ -327,12 +334,14 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
     khash = kernel_hash()
     kernel = {"moe": "rfp2_moe_gemv", "gemm": "rfp2_gemm", "gemm_f16": "rfp2_gemm_f16",
               "moe_tokens": f"{M} x rfp2_moe_gemv" if per_token else "rfp2_moe_gemv_tokens",
+              "moe_gemm": "rfp2_moe_gemm (sort + grouped GEMM)",
               }.get(cfg["op"], "rfp2_gemv")
     if one:
         kernel = "rfp2_quant_moe_gemv" if cfg["op"] == "moe" else "rfp2_quant_gemv"
-    if cfg["op"] in ("gemm", "gemm_f16"):
+    if cfg["op"] in ("gemm", "gemm_f16", "moe_gemm"):
         value = alg["ops"] / (ms_step * 1e-3) / 1e12
-        unit, metric = "TOPS", "ROCmFP2 M=512 GEMM int8 TOPS"
+        unit, metric = "TOPS", ("ROCmFP2 prompt-batch MoE GEMM int8 TOPS"
+                                if cfg["op"] == "moe_gemm" else "ROCmFP2 M=512 GEMM int8 TOPS")
         achieved = alg["ops"] / (kern_ms * 1e-3) / 1e12
         # the contraction's own dtype sets the peak: int8 5.0 POP/s, fp16 2.5 PFLOP/s
         peak = I8_PEAK_TOPS if cfg["op"] == "gemm" else F16_PEAK_TFLOPS
@@ -348,9 +357,9 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
                 kernel_us=kern_ms * 1e3, algorithmic_bytes=alg["product_bytes"],
                 algorithmic_ops=alg["ops"])
     config = {"workload": workload, "M": M, "N": N, "K": K}
-    if cfg["op"] in ("moe", "moe_tokens"):
+    if cfg["op"] in ("moe", "moe_tokens", "moe_gemm"):
         config.update(experts=cfg["E"], top_k=cfg["top_k"])
-    if cfg["op"] == "moe_tokens":
+    if cfg["op"] in ("moe_tokens", "moe_gemm"):
         config.update(tokens=M, expert_share=cfg["share"])
     config.update(weight_copies=copies, weight_bytes_per_copy=per_copy,
                   step=kernel if one else "rfp2_quantize_acts + " + kernel,

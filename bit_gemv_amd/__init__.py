@@ -38,6 +38,10 @@ _SIGNATURES = {
                        _c_p, _c_p], ctypes.c_int),
     "rfp2_moe_gemv_tokens": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_i64, _c_p, _c_p,
                               _c_p, _c_p, _c_p], ctypes.c_int),
+    "rfp2_moe_sort": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p], ctypes.c_int),
+    "rfp2_moe_gemm_workspace_bytes": ([_c_i64, _c_i64, _c_i64], ctypes.c_size_t),
+    "rfp2_moe_gemm": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p,
+                       _c_p, _c_p, ctypes.c_size_t, _c_p], ctypes.c_int),
     "rfp2_quant_gemv": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p], ctypes.c_int),
     "rfp2_quant_moe_gemv": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p,
                              _c_p, _c_p, _c_p], ctypes.c_int),
@@ -189,6 +193,35 @@ def rfp2_moe_gemv_tokens(w, E: int, N: int, K: int, ids, T: int, top_k: int, q, 
         _ptr(ids, torch.int32, T * top_k, "ids"), T, top_k,
         _ptr(q, torch.int8, T * K, "q"), _ptr(d, torch.float32, T * _blocks(K), "d"),
         _ptr(y, torch.float32, T * top_k * N, "y"), errp, _stream(stream)))
+
+
+def rfp2_moe_sort(ids, S: int, E: int, offsets, order, err=None, stream=None) -> None:
+    import torch
+    errp = None if err is None else _ptr(err, torch.int32, 1, "err")
+    _check("rfp2_moe_sort", lib().rfp2_moe_sort(
+        _ptr(ids, torch.int32, S, "ids"), S, E, _ptr(offsets, torch.int32, E + 1, "offsets"),
+        _ptr(order, torch.int32, S, "order"), errp, _stream(stream)))
+
+
+def rfp2_moe_gemm_workspace_bytes(E: int, T: int, top_k: int) -> int:
+    return int(lib().rfp2_moe_gemm_workspace_bytes(E, T, top_k))
+
+
+def rfp2_moe_gemm(w, E: int, N: int, K: int, ids, T: int, top_k: int, q, d, y, err=None,
+                  workspace=None, stream=None) -> None:
+    """workspace: a uint8 GPU tensor of at least rfp2_moe_gemm_workspace_bytes
+    bytes; when None, one is allocated for this call."""
+    import torch
+    need = rfp2_moe_gemm_workspace_bytes(E, T, top_k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=y.device)
+    errp = None if err is None else _ptr(err, torch.int32, 1, "err")
+    _check("rfp2_moe_gemm", lib().rfp2_moe_gemm(
+        _ptr(w, torch.uint8, E * N * _blocks(K) * 10, "w"), E, N, K,
+        _ptr(ids, torch.int32, T * top_k, "ids"), T, top_k,
+        _ptr(q, torch.int8, T * K, "q"), _ptr(d, torch.float32, T * _blocks(K), "d"),
+        _ptr(y, torch.float32, T * top_k * N, "y"), errp,
+        _ptr(workspace, torch.uint8, need, "workspace"), workspace.numel(), _stream(stream)))
 
 
 def rfp2_quant_gemv(w, N: int, K: int, a, q, d, y, stream=None) -> None:

@@ -19,12 +19,17 @@
 // gfx950 mapping: workgroup tile 128 tokens x 128 rows, four waves of 64 x 64
 // (2 x 2 tiles of v_mfma_f32_32x32x16_f16), K stage of 2 blocks, two LDS
 // buffers with register prefetch of the next stage, XCD-aware tile order
-// (as gemm.hip).  Within each 16-weight half the k order in LDS is
+// (as gemm.hip).  The routed form (tokens sorted by expert, a prompt batch
+// through the routed experts) uses 64-token tiles, each inside one expert's
+// slots, gathering its tokens' activation rows and scattering its outputs to
+// their slots' rows.  Within each 16-weight half the k order in LDS is
 // 0,4, 1,5, 2,6, 3,7, 8,12, 9,13, 10,14, 11,15 for weights and activations
 // alike (the order the decode produces cheaply); a dot product over the half
 // does not depend on it.
 #include "rfp2_device.h"
 #include "rfp2_internal.h"
+
+#include <climits>
 
 namespace rfp2 {
 
@@ -33,13 +38,16 @@ namespace {
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
-constexpr int BM = 128;
 constexpr int BN = 128;
 constexpr int BKB = 2;                          // blocks per LDS stage
 constexpr int kRowBytes = BKB * 32 * 2 + 16;    // fp16 row of a stage + pad (144)
 constexpr int kXcds = 8;
 
+// TM: 32-token MFMA tiles per wave along the tokens; a workgroup's four waves
+// are 2 (tokens) x 2 (rows), so it covers BM = 64 * TM tokens x 128 rows.
+template <int TM>
 struct __align__(16) StageF16 {
+  static constexpr int BM = 64 * TM;
   uint8_t wh[BN * kRowBytes];      // fp16 weights (level * scale)
   uint8_t ah[BM * kRowBytes];      // fp16 activations
   float ad[BKB][BM];               // activation scale per (block, token)
@@ -111,31 +119,34 @@ __device__ __forceinline__ void act_half_f16(const uint32_t (&X)[4], uint32_t (&
   }
 }
 
-__device__ __forceinline__ void fetch(PrefetchF16& f, const uint8_t* __restrict__ w,
-                                      const int8_t* __restrict__ q,
-                                      const float* __restrict__ d, int64_t row_bytes,
-                                      int K, int nb, int kb, int tid, int n0, int m0,
-                                      int N, int M) {
-  // thread -> (weight row tid / 2, block tid % 2 of the stage); both threads
-  // of a row load the dword-aligned 20-byte pair of blocks
-  const int wrow = tid >> 1;
-  const int n = n0 + wrow < N ? n0 + wrow : 0;   // rows past the end read row 0
-  const uint32_t* src =
-      reinterpret_cast<const uint32_t*>(w + (int64_t)n * row_bytes + (int64_t)kb * 10);
+// The rows a thread loads, fixed for the whole tile: its weight row (thread
+// -> row tid / 2; both threads of a row load the dword-aligned 20-byte pair
+// of blocks of the stage) and its token's activation row (thread -> token
+// tid / 2, 32-byte block tid % 2 of the stage; only the first 2 * BM threads
+// load activations).
+struct RowPtrs {
+  const uint8_t* w;
+  const int8_t* q;
+  const float* d;
+};
+
+__device__ __forceinline__ void fetch(PrefetchF16& f, const RowPtrs& r, int kb, int tid,
+                                      bool acts) {
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(r.w + (int64_t)kb * 10);
 #pragma unroll
   for (int i = 0; i < 5; ++i) f.wd[i] = src[i];
-  // thread -> (token tid / 2, 32-byte block tid % 2 of the stage)
-  const int arow = tid >> 1, ablk = tid & 1;
-  const int m = m0 + arow < M ? m0 + arow : 0;
-  const uint4* asrc =
-      reinterpret_cast<const uint4*>(q + (int64_t)m * K + (int64_t)(kb + ablk) * 32);
-  f.a[0] = asrc[0];
-  f.a[1] = asrc[1];
-  f.d = d[(int64_t)m * nb + kb + ablk];
+  if (acts) {
+    const int ablk = tid & 1;
+    const uint4* asrc = reinterpret_cast<const uint4*>(r.q + (int64_t)(kb + ablk) * 32);
+    f.a[0] = asrc[0];
+    f.a[1] = asrc[1];
+    f.d = r.d[kb + ablk];
+  }
 }
 
-__device__ __forceinline__ void stage_to_lds(const PrefetchF16& f, StageF16& st, int tid,
-                                             float fix) {
+template <int TM>
+__device__ __forceinline__ void stage_to_lds(const PrefetchF16& f, StageF16<TM>& st, int tid,
+                                             float fix, bool acts) {
   const int wrow = tid >> 1, blk = tid & 1;
   // block 0 of the pair is dwords 0..2 (scales in the low half of dword 2),
   // block 1 starts 16 bits into dword 2; selects and funnel shifts, no branch
@@ -156,85 +167,157 @@ __device__ __forceinline__ void stage_to_lds(const PrefetchF16& f, StageF16& st,
   dst[2] = make_uint4(h1[0], h1[1], h1[2], h1[3]);
   dst[3] = make_uint4(h1[4], h1[5], h1[6], h1[7]);
 
-  const int arow = tid >> 1, ablk = tid & 1;
-  uint4* adst = reinterpret_cast<uint4*>(st.ah + arow * kRowBytes + ablk * 64);
+  if (acts) {
+    const int arow = tid >> 1, ablk = tid & 1;
+    uint4* adst = reinterpret_cast<uint4*>(st.ah + arow * kRowBytes + ablk * 64);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t X[4] = {f.a[h].x, f.a[h].y, f.a[h].z, f.a[h].w};
-    uint32_t o[8];
-    act_half_f16(X, o);
-    adst[2 * h] = make_uint4(o[0], o[1], o[2], o[3]);
-    adst[2 * h + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t X[4] = {f.a[h].x, f.a[h].y, f.a[h].z, f.a[h].w};
+      uint32_t o[8];
+      act_half_f16(X, o);
+      adst[2 * h] = make_uint4(o[0], o[1], o[2], o[3]);
+      adst[2 * h + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+    st.ad[ablk][arow] = f.d;
   }
-  st.ad[ablk][arow] = f.d;
 }
 
-// Block sums of the stage in sm for this wave's 64 x 64 (row x token) tile,
-// rescaled by the activation scales and added to acc.  MFMA operand A is the
-// weights (i = row), B the activations (j = token), so every lane holds one
-// token's column of each 32 x 32 tile and the activation scale of a block is
-// one register per tile.
-__device__ __forceinline__ void compute_stage(const StageF16& st, int lane, int wm, int wn,
-                                              v16f (&acc)[2][2]) {
+// Block sums of the stage in sm for this wave's 64 x (32 * TM) (row x token)
+// tile, rescaled by the activation scales and added to acc.  MFMA operand A
+// is the weights (i = row), B the activations (j = token), so every lane
+// holds one token's column of each 32 x 32 tile and the activation scale of
+// a block is one register per tile.
+template <int TM>
+__device__ __forceinline__ void compute_stage(const StageF16<TM>& st, int lane, int wm, int wn,
+                                              v16f (&acc)[2][TM]) {
   const int koff = 16 * (lane >> 5);            // bytes: 8 fp16 per lane half
 #pragma unroll
   for (int blk = 0; blk < BKB; ++blk) {
-    v8h a[2][2], b[2][2];                       // [half][tile]
-    float dd[2];
+    v8h a[2][2], b[2][TM];                      // [half][tile]
+    float dd[TM];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < 2; ++h)
         a[h][t] = *reinterpret_cast<const v8h*>(
             st.wh + (wn * 64 + t * 32 + (lane & 31)) * kRowBytes + blk * 64 + h * 32 + koff);
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
         b[h][t] = *reinterpret_cast<const v8h*>(
-            st.ah + (wm * 64 + t * 32 + (lane & 31)) * kRowBytes + blk * 64 + h * 32 + koff);
-      }
-      dd[t] = st.ad[blk][wm * 64 + t * 32 + (lane & 31)];
+            st.ah + (wm * 32 * TM + t * 32 + (lane & 31)) * kRowBytes + blk * 64 + h * 32 +
+            koff);
+      dd[t] = st.ad[blk][wm * 32 * TM + t * 32 + (lane & 31)];
     }
-    // all four tiles' block sums first, then the rescale, so that the FMAs
-    // of a tile do not wait on the matrix-core latency of that same tile
-    v16f c[2][2];
+    // all tiles' block sums first, then the rescale, so that the FMAs of a
+    // tile do not wait on the matrix-core latency of that same tile
+    v16f c[2][TM];
 #pragma unroll
     for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
-      for (int tm = 0; tm < 2; ++tm) {
+      for (int tm = 0; tm < TM; ++tm) {
         c[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[0][tn], b[0][tm], v16f{}, 0, 0, 0);
         c[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[1][tn], b[1][tm], c[tn][tm], 0, 0, 0);
       }
 #pragma unroll
     for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
-      for (int tm = 0; tm < 2; ++tm)
+      for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[tn][tm][r] = fmaf(dd[tm], c[tn][tm][r], acc[tn][tm][r]);
   }
 }
 
-__global__ __launch_bounds__(256, 2) void gemm_f16_kernel(
-    const uint8_t* __restrict__ w, int N, int K, const int8_t* __restrict__ q,
-    const float* __restrict__ d, int M, float* __restrict__ y, int m_tiles,
-    int tiles) {
-  __shared__ StageF16 sm[2];
+struct GemmF16Params {
+  const uint8_t* w;   // dense: [N] rows; routed: E experts of [N] rows
+  int N, K;
+  const int8_t* q;
+  const float* d;
+  float* y;
+  // dense product
+  int M, m_tiles, tiles;
+  // routed product (tokens sorted by expert): expert e's slots are
+  // order[offsets[e] .. offsets[e+1]); its 64-token tiles are numbered from
+  // tile_start[e]; tile_start[E] tiles in all
+  const int32_t* offsets;
+  const int32_t* tile_start;
+  const int32_t* order;
+  int E, top_k, n_tiles;
+};
+
+// Expert owning routed tile i: the last e with tile_start[e] <= i (the array
+// is non-decreasing; an expert with no slots has an empty range).  Two
+// wave-wide probes of at most 64 entries each (E + 1 <= 64 * 64).
+__device__ __forceinline__ int expert_of_tile(const int32_t* tile_start, int E, int i,
+                                              int lane) {
+  const int chunk = (E + 64) >> 6;              // ceil((E + 1) / 64)
+  int idx = lane * chunk;
+  int v = idx <= E ? tile_start[idx] : INT_MAX;
+  const int seg = 63 - __clzll(__ballot(v <= i));   // lane 0 always qualifies
+  idx = seg * chunk + lane;
+  v = (lane < chunk && idx <= E) ? tile_start[idx] : INT_MAX;
+  return seg * chunk + (63 - __clzll(__ballot(v <= i)));
+}
+
+template <int TM, bool MOE>
+__global__ __launch_bounds__(256, 2) void gemm_f16_kernel(GemmF16Params p) {
+  constexpr int BM = 64 * TM;
+  __shared__ StageF16<TM> sm[2];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  int tile = blockIdx.x;
-  if (tiles % kXcds == 0) tile = (blockIdx.x % kXcds) * (tiles / kXcds) + blockIdx.x / kXcds;
-  const int mt = tile % m_tiles;
-  const int nt = tile / m_tiles;
-  const int m0 = mt * BM, n0 = nt * BN;
+  const int N = p.N, K = p.K;
   const int64_t row_bytes = (int64_t)(K / 32) * 10;
   const int nb = K / 32;
   const int stages = nb / BKB;
   const float fix = scale_fix();
 
-  v16f acc[2][2];                               // [row tile][token tile]
+  // tile -> (tokens, rows).  Dense: XCD-aware order over (m, n) tiles as in
+  // gemm.hip.  Routed: workgroup b runs on XCD b % 8; token tile i goes to
+  // XCD i % 8 with all of its row tiles, so an XCD's L2 holds the tile's
+  // gathered activations for every row tile; workgroups past the last tile
+  // leave at once (the grid is sized for the worst routing).
+  int n0, rows, m0 = 0, start = 0;
+  const uint8_t* wbase = p.w;
+  if constexpr (MOE) {
+    const int x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+    const int i = kXcds * (k / p.n_tiles) + x;
+    if (i >= p.tile_start[p.E]) return;
+    const int e = expert_of_tile(p.tile_start, p.E, i, lane);
+    start = p.offsets[e] + (i - p.tile_start[e]) * BM;
+    rows = min(BM, p.offsets[e + 1] - start);
+    n0 = (k % p.n_tiles) * BN;
+    wbase += (int64_t)e * N * row_bytes;
+  } else {
+    int tile = blockIdx.x;
+    if (p.tiles % kXcds == 0)
+      tile = (blockIdx.x % kXcds) * (p.tiles / kXcds) + blockIdx.x / kXcds;
+    const int mt = tile % p.m_tiles;
+    m0 = mt * BM;
+    n0 = (tile / p.m_tiles) * BN;
+    rows = min(BM, p.M - m0);
+  }
+
+  // this thread's load rows; rows past the end re-read a valid row (the
+  // results are never stored)
+  const bool acts = tid < 2 * BM;               // uniform per wave
+  RowPtrs rp;
+  {
+    const int wn_row = n0 + (tid >> 1) < N ? n0 + (tid >> 1) : 0;
+    rp.w = wbase + (int64_t)wn_row * row_bytes;
+    const int r = min(tid >> 1, rows - 1);
+    const int token = MOE ? p.order[start + r] / p.top_k : m0 + r;
+    rp.q = p.q + (int64_t)token * K;
+    rp.d = p.d + (int64_t)token * nb;
+  }
+
+  v16f acc[2][TM];                              // [row tile][token tile]
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+    for (int j = 0; j < TM; ++j) acc[i][j] = v16f{};
 
   // Software pipeline: iteration s computes stage s from one LDS buffer while
   // it expands stage s+1 (already in registers) into the other buffer and
@@ -244,29 +327,30 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_kernel(
   // peeled off and the load of a stage past the end re-reads the last one),
   // so the matrix-core and vector work of an iteration can be interleaved.
   PrefetchF16 f;
-  fetch(f, w, q, d, row_bytes, K, nb, 0, tid, n0, m0, N, M);
-  stage_to_lds(f, sm[0], tid, fix);
-  fetch(f, w, q, d, row_bytes, K, nb, stages > 1 ? BKB : 0, tid, n0, m0, N, M);
+  fetch(f, rp, 0, tid, acts);
+  stage_to_lds(f, sm[0], tid, fix, acts);
+  fetch(f, rp, stages > 1 ? BKB : 0, tid, acts);
   __syncthreads();
   for (int s = 0; s + 1 < stages; ++s) {
     compute_stage(sm[s & 1], lane, wm, wn, acc);
-    stage_to_lds(f, sm[(s + 1) & 1], tid, fix);
+    stage_to_lds(f, sm[(s + 1) & 1], tid, fix, acts);
     const int next = s + 2 < stages ? s + 2 : stages - 1;
-    fetch(f, w, q, d, row_bytes, K, nb, next * BKB, tid, n0, m0, N, M);
+    fetch(f, rp, next * BKB, tid, acts);
     __syncthreads();
   }
   compute_stage(sm[(stages - 1) & 1], lane, wm, wn, acc);
 
-  // lane -> token m, register r -> row n; rows n..n+3 of a register group are
+  // lane -> token, register r -> row n; rows n..n+3 of a register group are
   // contiguous in y, so whole groups go out as one 16-byte store
-  const bool vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+  const bool vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
 #pragma unroll
-  for (int tn = 0; tn < 2; ++tn)
+  for (int tm = 0; tm < TM; ++tm) {
+    const int m = wm * 32 * TM + tm * 32 + (lane & 31);
+    if (m >= rows) continue;
+    const int out_row = MOE ? p.order[start + m] : m0 + m;
+    float* yr = p.y + (int64_t)out_row * N;
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm) {
-      const int m = m0 + wm * 64 + tm * 32 + (lane & 31);
-      if (m >= M) continue;
-      float* yr = y + (int64_t)m * N;
+    for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int n = n0 + wn * 64 + tn * 32 + 8 * g + 4 * (lane >> 5);
@@ -280,18 +364,52 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_kernel(
             if (n + e < N) yr[n + e] = v[4 * g + e];
         }
       }
-    }
+  }
 }
 
 }  // namespace
 
 hipError_t launch_gemm_f16(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
                            const float* d, int64_t M, float* y, hipStream_t stream) {
-  const int m_tiles = (int)((M + BM - 1) / BM);
+  constexpr int BM = StageF16<2>::BM;
+  GemmF16Params p{};
+  p.w = w; p.N = (int)N; p.K = (int)K; p.q = q; p.d = d; p.y = y; p.M = (int)M;
+  p.m_tiles = (int)((M + BM - 1) / BM);
   const int n_tiles = (int)((N + BN - 1) / BN);
-  const int tiles = m_tiles * n_tiles;
-  hipLaunchKernelGGL(gemm_f16_kernel, dim3((uint32_t)tiles), dim3(256), 0, stream, w,
-                     (int)N, (int)K, q, d, (int)M, y, m_tiles, tiles);
+  p.tiles = p.m_tiles * n_tiles;
+  hipLaunchKernelGGL((gemm_f16_kernel<2, false>), dim3((uint32_t)p.tiles), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+int moe_gemm_tile_tokens() { return StageF16<1>::BM; }
+
+// Workgroups of the routed product: every row tile of the most token tiles
+// any routing of S slots over E experts can need (at most one partly filled
+// tile per expert that has slots), rounded up to whole rounds of the XCDs.
+int64_t moe_gemm_max_grid(int64_t E, int64_t N, int64_t S) {
+  constexpr int BM = StageF16<1>::BM;
+  const int64_t max_tiles = (S + BM - 1) / BM + std::min<int64_t>(E, S);
+  const int64_t per_xcd = (max_tiles + kXcds - 1) / kXcds;
+  return (int64_t)kXcds * ((N + BN - 1) / BN) * per_xcd;
+}
+
+// Routed product over slots already sorted by expert (offsets, tile_start,
+// order as written by the sort kernel with tile rows = moe_gemm_tile_tokens()).
+hipError_t launch_moe_gemm_sorted(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                                  const int32_t* offsets, const int32_t* tile_start,
+                                  const int32_t* order, int64_t S, int64_t top_k,
+                                  const int8_t* q, const float* d, float* y,
+                                  hipStream_t stream) {
+  constexpr int BM = StageF16<1>::BM;
+  GemmF16Params p{};
+  p.w = w; p.N = (int)N; p.K = (int)K; p.q = q; p.d = d; p.y = y;
+  p.offsets = offsets; p.tile_start = tile_start; p.order = order;
+  p.E = (int)E; p.top_k = (int)top_k;
+  p.n_tiles = (int)((N + BN - 1) / BN);
+  const int64_t grid = moe_gemm_max_grid(E, N, S);
+  hipLaunchKernelGGL((gemm_f16_kernel<1, true>), dim3((uint32_t)grid), dim3(256), 0, stream,
+                     p);
   return hipGetLastError();
 }
 

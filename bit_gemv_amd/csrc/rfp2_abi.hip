@@ -8,6 +8,7 @@ namespace {
 
 constexpr int64_t kMaxRows = int64_t(1) << 30;     // row and token counts
 constexpr int64_t kMaxGemvK = 32768;               // staged activations fit LDS
+constexpr int64_t kMaxSortSlots = int64_t(1) << 24;  // routed slots of one sort
 
 bool aligned(const void* p, uintptr_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
@@ -137,6 +138,43 @@ rfp2_status rfp2_moe_gemv_tokens(const uint8_t* w, int64_t E, int64_t N, int64_t
   (void)hipGetLastError();
   return from_hip(
       rfp2::launch_moe_gemv_tokens(w, E, N, K, ids, T, top_k, q, d, y, err, stream));
+}
+
+rfp2_status rfp2_moe_sort(const int32_t* ids, int64_t S, int64_t E, int32_t* offsets,
+                          int32_t* order, int32_t* err, hipStream_t stream) {
+  if (!ids || !offsets || !order) return RFP2_E_NULL;
+  if (S < 1 || S > kMaxSortSlots || E < 1 || E > rfp2::kMaxSortExperts) return RFP2_E_SHAPE;
+  if (!aligned(ids, 4) || !aligned(offsets, 4) || !aligned(order, 4) ||
+      (err && !aligned(err, 4)))
+    return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(rfp2::launch_moe_sort(ids, S, E, 0, offsets, nullptr, order, err, nullptr,
+                                        0, stream));
+}
+
+size_t rfp2_moe_gemm_workspace_bytes(int64_t E, int64_t T, int64_t top_k) {
+  if (E < 1 || E > rfp2::kMaxSortExperts || T < 1 || top_k < 1 || T > kMaxSortSlots ||
+      top_k > kMaxSortSlots || T * top_k > kMaxSortSlots)
+    return 0;
+  return rfp2::moe_gemm_workspace_bytes(E, T * top_k);
+}
+
+rfp2_status rfp2_moe_gemm(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                          const int32_t* ids, int64_t T, int64_t top_k, const int8_t* q,
+                          const float* d, float* y, int32_t* err, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  if (!w || !ids || !q || !d || !y || !workspace) return RFP2_E_NULL;
+  const size_t need = rfp2_moe_gemm_workspace_bytes(E, T, top_k);
+  if (need == 0 || N < 1 || N > kMaxRows || K < 256 || K % 256 != 0 ||
+      K > (int64_t(1) << 24) || workspace_bytes < need)
+    return RFP2_E_SHAPE;
+  if (rfp2::moe_gemm_max_grid(E, N, T * top_k) > (int64_t(1) << 31) - 1) return RFP2_E_SHAPE;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(d, 4) || !aligned(y, 4) ||
+      !aligned(ids, 4) || !aligned(workspace, 256) || (err && !aligned(err, 4)))
+    return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(rfp2::launch_moe_gemm(w, E, N, K, ids, T, top_k, q, d, y, err, workspace,
+                                        stream));
 }
 
 rfp2_status rfp2_quant_gemv(const uint8_t* w, int64_t N, int64_t K, const float* a,

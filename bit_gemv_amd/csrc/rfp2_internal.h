@@ -10,6 +10,7 @@
 namespace rfp2 {
 
 constexpr int64_t kMaxGrid = 1 << 20;   // workgroups per launch (grid-stride beyond)
+constexpr int kMaxSortExperts = 2048;   // experts of a grouped (sorted) routed product
 
 hipError_t launch_quantize_acts(const float* a, int64_t M, int64_t K, int8_t* q,
                                 float* d, hipStream_t stream);
@@ -35,6 +36,21 @@ hipError_t launch_gemm(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
                        const float* d, int64_t M, float* y, hipStream_t stream);
 hipError_t launch_gemm_f16(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
                            const float* d, int64_t M, float* y, hipStream_t stream);
+hipError_t launch_moe_sort(const int32_t* ids, int64_t S, int64_t E, int64_t tile_rows,
+                           int32_t* offsets, int32_t* tile_start, int32_t* order,
+                           int32_t* err, float* y, int64_t N, hipStream_t stream);
+int moe_gemm_tile_tokens();
+hipError_t launch_moe_gemm_sorted(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                                  const int32_t* offsets, const int32_t* tile_start,
+                                  const int32_t* order, int64_t S, int64_t top_k,
+                                  const int8_t* q, const float* d, float* y,
+                                  hipStream_t stream);
+size_t moe_gemm_workspace_bytes(int64_t E, int64_t S);
+int64_t moe_gemm_max_grid(int64_t E, int64_t N, int64_t S);
+hipError_t launch_moe_gemm(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                           const int32_t* ids, int64_t T, int64_t top_k, const int8_t* q,
+                           const float* d, float* y, int32_t* err, void* workspace,
+                           hipStream_t stream);
 hipError_t launch_debug_decode(const uint8_t* w, int64_t N, int64_t K,
                                int8_t* codes, float* scales, hipStream_t stream);
 hipError_t launch_debug_half_dots(const uint8_t* w, int64_t N, int64_t K,

@@ -41,6 +41,7 @@
 #ifndef RFP2_H
 #define RFP2_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -187,6 +188,57 @@ rfp2_status rfp2_moe_gemv_tokens(const uint8_t* w, int64_t E, int64_t N, int64_t
                                  const int32_t* ids, int64_t T, int64_t top_k,
                                  const int8_t* q, const float* d, float* y, int32_t* err,
                                  hipStream_t stream);
+
+/*
+ * rfp2_moe_sort -- the routed slots grouped by expert, the token order of a
+ * prompt batch through the routed experts ("04 · Measured evidence" and
+ * "07 · Recipe decision": the method's gain is prefill on large expert
+ * tensors; a prefill product takes each expert's tokens together).
+ *   ids     [S] int32 on the device: slot s (token s / top_k of a batch) is
+ *           routed to expert ids[s].
+ *   offsets [E+1] int32 (written): expert e's slots are
+ *           order[offsets[e] .. offsets[e+1]); offsets[E] = the routed slots.
+ *   order   [S] int32 (written up to offsets[E]): every slot whose id lies in
+ *           [0, E), grouped by expert in expert order, increasing slot order
+ *           inside an expert (the stable order: deterministic).
+ *   err     nullable device int32: set to 1 when an id lies outside [0, E)
+ *           (such slots are left out; never cleared by the call).
+ * One workgroup; suited to the few thousand slots of a prompt batch.
+ * Requires 1 <= S <= 2^24, 1 <= E <= 2048; all pointers 4-byte aligned.
+ */
+rfp2_status rfp2_moe_sort(const int32_t* ids, int64_t S, int64_t E, int32_t* offsets,
+                          int32_t* order, int32_t* err, hipStream_t stream);
+
+/*
+ * rfp2_moe_gemm_workspace_bytes -- device bytes rfp2_moe_gemm needs as
+ * workspace for E experts and T * top_k slots (0 when the sizes are out of
+ * range).
+ */
+size_t rfp2_moe_gemm_workspace_bytes(int64_t E, int64_t T, int64_t top_k);
+
+/*
+ * rfp2_moe_gemm -- routed-expert products for a prompt batch of T tokens on
+ * the matrix cores: the slots are sorted by expert (rfp2_moe_sort), then each
+ * expert's slots are cut into tiles of 64 tokens and multiplied with that
+ * expert's weights as rfp2_gemm_f16 multiplies a dense batch (exact fp16
+ * operands, one rescale per output and block).
+ *   w    E experts back to back, each [N][K/32][10] bytes; 16-byte aligned.
+ *   ids  [T][top_k] int32 on the device; slot s = t * top_k + j.
+ *   q, d [T][K] int8 (16-byte aligned) and [T][K/32] fp32.
+ *   y    [T][top_k][N] fp32: row s = expert ids[s] applied to token s / top_k
+ *        (NaN for an id outside [0, E), and *err = 1 as rfp2_moe_gemv).
+ *   workspace  device memory of at least rfp2_moe_gemm_workspace_bytes(E, T,
+ *        top_k) bytes, 256-byte aligned, owned by the caller; overwritten.
+ *        Calls that share a workspace must not overlap in time.
+ * Each output is computed independently of which other slots share its
+ * tile, so y does not depend on the routing of the other tokens.
+ * Requires 1 <= E <= 2048, N >= 1, T >= 1, top_k >= 1, T * top_k <= 2^24,
+ * 256 <= K <= 2^24, K % 256 == 0.
+ */
+rfp2_status rfp2_moe_gemm(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                          const int32_t* ids, int64_t T, int64_t top_k, const int8_t* q,
+                          const float* d, float* y, int32_t* err, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
 
 /*
  * rfp2_quant_gemv -- one token end to end: quantizes the fp32 activations a

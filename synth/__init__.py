@@ -27,6 +27,11 @@ WORKLOADS = {
     # before: tokens grouped per expert, each expert decoded once
     "moe_128x1536x4096_top8_t4": dict(op="moe_tokens", M=4, E=128, top_k=8, N=1536,
                                       K=4096, sigma=0.02, wseed=0, share=0.5),
+    # the same bank for a 512-token prompt: every token routed to 8 distinct
+    # experts, independently of the others (4096 slots, ~32 per expert)
+    "moe_gemm_128x1536x4096_top8_t512": dict(op="moe_gemm", M=512, E=128, top_k=8,
+                                             N=1536, K=4096, sigma=0.02, wseed=0,
+                                             share=0.0),
     # large layer GEMV (25.0 MiB of ROCmFP2 weights) at 1 and 4 tokens
     "gemv_16384x5120": dict(op="gemv", M=1, N=16384, K=5120, sigma=0.015,
                             wseed=0),

@@ -64,6 +64,32 @@ def test_gemm_moe_quantize_argument_checks():
     assert L.rfp2_debug_half_dots(P, 1, 64, P, 0, P, None) == rf.RFP2_E_SHAPE
 
 
+def test_moe_sort_and_moe_gemm_argument_checks():
+    L = rf.lib()
+    assert L.rfp2_moe_sort(None, 10, 4, P, P, None, None) == rf.RFP2_E_NULL
+    assert L.rfp2_moe_sort(P, 0, 4, P, P, None, None) == rf.RFP2_E_SHAPE
+    assert L.rfp2_moe_sort(P, 10, 0, P, P, None, None) == rf.RFP2_E_SHAPE
+    assert L.rfp2_moe_sort(P, 10, 2049, P, P, None, None) == rf.RFP2_E_SHAPE
+    assert L.rfp2_moe_sort(P, (1 << 24) + 1, 4, P, P, None, None) == rf.RFP2_E_SHAPE
+    assert L.rfp2_moe_sort(P, 10, 4, P + 2, P, None, None) == rf.RFP2_E_ALIGN
+    need = L.rfp2_moe_gemm_workspace_bytes(8, 512, 8)
+    assert need >= 4 * (2 * 9 + 4096) and need % 256 == 0
+    assert L.rfp2_moe_gemm_workspace_bytes(0, 1, 1) == 0
+    assert L.rfp2_moe_gemm_workspace_bytes(2049, 1, 1) == 0
+    assert L.rfp2_moe_gemm_workspace_bytes(8, 1 << 20, 17) == 0      # above 2^24 slots
+
+    def gemm(E=8, N=64, K=256, T=512, top_k=8, ws=P, ws_bytes=need, q=P, err=None):
+        return L.rfp2_moe_gemm(P, E, N, K, P, T, top_k, q, P, P, err, ws, ws_bytes, None)
+    assert gemm(ws=None) == rf.RFP2_E_NULL
+    assert gemm(ws_bytes=need - 4) == rf.RFP2_E_SHAPE
+    assert gemm(K=320) == rf.RFP2_E_SHAPE
+    assert gemm(N=0) == rf.RFP2_E_SHAPE
+    assert gemm(E=4096) == rf.RFP2_E_SHAPE
+    assert gemm(ws=P + 64) == rf.RFP2_E_ALIGN                  # workspace: 256 bytes
+    assert gemm(q=MIS) == rf.RFP2_E_ALIGN
+    assert gemm(err=P + 1) == rf.RFP2_E_ALIGN
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(16, dtype=torch.uint8)
