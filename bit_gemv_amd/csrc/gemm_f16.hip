@@ -20,9 +20,9 @@
 // (2 x 2 tiles of v_mfma_f32_32x32x16_f16), K stage of 2 blocks, two LDS
 // buffers with register prefetch of the next stage, XCD-aware tile order
 // (as gemm.hip).  The routed form (tokens sorted by expert, a prompt batch
-// through the routed experts) uses 64-token tiles, each inside one expert's
-// slots, gathering its tokens' activation rows and scattering its outputs to
-// their slots' rows.  Within each 16-weight half the k order in LDS is
+// through the routed experts) has a kernel of its own below
+// (moe_gemm_kernel): 64-token tiles, each inside one expert's slots, with
+// the weights decoded straight into registers.  Within each 16-weight half the k order in LDS is
 // 0,4, 1,5, 2,6, 3,7, 8,12, 9,13, 10,14, 11,15 for weights and activations
 // alike (the order the decode produces cheaply); a dot product over the half
 // does not depend on it.
@@ -260,7 +260,7 @@ __device__ __forceinline__ int expert_of_tile(const int32_t* tile_start, int E, 
   return seg * chunk + (63 - __clzll(__ballot(v <= i)));
 }
 
-template <int TM, bool MOE>
+template <int TM>
 __global__ __launch_bounds__(256, 2) void gemm_f16_kernel(GemmF16Params p) {
   constexpr int BM = 64 * TM;
   __shared__ StageF16<TM> sm[2];
@@ -274,31 +274,13 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_kernel(GemmF16Params p) {
   const int stages = nb / BKB;
   const float fix = scale_fix();
 
-  // tile -> (tokens, rows).  Dense: XCD-aware order over (m, n) tiles as in
-  // gemm.hip.  Routed: workgroup b runs on XCD b % 8; token tile i goes to
-  // XCD i % 8 with all of its row tiles, so an XCD's L2 holds the tile's
-  // gathered activations for every row tile; workgroups past the last tile
-  // leave at once (the grid is sized for the worst routing).
-  int n0, rows, m0 = 0, start = 0;
-  const uint8_t* wbase = p.w;
-  if constexpr (MOE) {
-    const int x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
-    const int i = kXcds * (k / p.n_tiles) + x;
-    if (i >= p.tile_start[p.E]) return;
-    const int e = expert_of_tile(p.tile_start, p.E, i, lane);
-    start = p.offsets[e] + (i - p.tile_start[e]) * BM;
-    rows = min(BM, p.offsets[e + 1] - start);
-    n0 = (k % p.n_tiles) * BN;
-    wbase += (int64_t)e * N * row_bytes;
-  } else {
-    int tile = blockIdx.x;
-    if (p.tiles % kXcds == 0)
-      tile = (blockIdx.x % kXcds) * (p.tiles / kXcds) + blockIdx.x / kXcds;
-    const int mt = tile % p.m_tiles;
-    m0 = mt * BM;
-    n0 = (tile / p.m_tiles) * BN;
-    rows = min(BM, p.M - m0);
-  }
+  // tile -> (tokens, rows): XCD-aware order over (m, n) tiles as in gemm.hip
+  int tile = blockIdx.x;
+  if (p.tiles % kXcds == 0)
+    tile = (blockIdx.x % kXcds) * (p.tiles / kXcds) + blockIdx.x / kXcds;
+  const int m0 = (tile % p.m_tiles) * BM;
+  const int n0 = (tile / p.m_tiles) * BN;
+  const int rows = min(BM, p.M - m0);
 
   // this thread's load rows; rows past the end re-read a valid row (the
   // results are never stored)
@@ -306,9 +288,8 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_kernel(GemmF16Params p) {
   RowPtrs rp;
   {
     const int wn_row = n0 + (tid >> 1) < N ? n0 + (tid >> 1) : 0;
-    rp.w = wbase + (int64_t)wn_row * row_bytes;
-    const int r = min(tid >> 1, rows - 1);
-    const int token = MOE ? p.order[start + r] / p.top_k : m0 + r;
+    rp.w = p.w + (int64_t)wn_row * row_bytes;
+    const int token = m0 + min(tid >> 1, rows - 1);
     rp.q = p.q + (int64_t)token * K;
     rp.d = p.d + (int64_t)token * nb;
   }
@@ -347,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_kernel(GemmF16Params p) {
   for (int tm = 0; tm < TM; ++tm) {
     const int m = wm * 32 * TM + tm * 32 + (lane & 31);
     if (m >= rows) continue;
-    const int out_row = MOE ? p.order[start + m] : m0 + m;
+    const int out_row = m0 + m;
     float* yr = p.y + (int64_t)out_row * N;
 #pragma unroll
     for (int tn = 0; tn < 2; ++tn)
@@ -367,6 +348,217 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_kernel(GemmF16Params p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Routed product (tokens sorted by expert).  A routed tile holds few tokens
+// (~32 per expert in a 512-token prompt), so the dense layout above would
+// move every decoded weight through LDS for little reuse.  Here each wave
+// owns 32 weight rows and decodes its MFMA operand A straight into
+// registers; only the activations go through LDS.  One 16-k MFMA step takes
+// eight weights of each half of a block (lanes 0-31: half 0, lanes 32-63:
+// half 1), so a lane decodes one half: the halves' scales are folded into
+// the operand, and the step's sum over both halves is still the block's
+// sum.  The activations are laid out to match: for token m and block b the
+// LDS row holds, per step j, half 0's eight values then half 1's.
+
+constexpr int kMoeWaves = 4;
+constexpr int kMoeRows = 32 * kMoeWaves;      // weight rows per workgroup
+constexpr int kMoeTokens = 64;                // slots per tile: two 32-token MFMA tiles
+constexpr int kMoeKB = 8;                     // blocks per activation stage
+constexpr int kMoeActRow = kMoeKB * 64 + 16;  // fp16 bytes of one token's stage (+ pad)
+
+struct __align__(16) MoeStage {
+  uint8_t ah[kMoeTokens * kMoeActRow];
+  float ad[kMoeKB][kMoeTokens];
+};
+
+// The 20-byte pair of blocks (2p, 2p + 1) of one weight row (named fields:
+// no indexing, which would put them in scratch memory).
+struct WPair {
+  uint32_t d0, d1, d2, d3, d4;
+};
+
+__device__ __forceinline__ void load_pair(WPair& w, const uint8_t* row, int kb) {
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(row + (int64_t)kb * 10);
+  w.d0 = src[0];
+  w.d1 = src[1];
+  w.d2 = src[2];
+  w.d3 = src[3];
+  w.d4 = src[4];
+}
+
+// This lane's half (kh) of block ODD of a pair, decoded to the two MFMA A
+// operands (steps 0 and 1) of the block.
+template <int ODD>
+__device__ __forceinline__ void decode_half(const WPair& w, int kh, float fix, v8h& a0,
+                                            v8h& a1) {
+  uint32_t x0, x1, sc;
+  if constexpr (ODD) {
+    x0 = __builtin_amdgcn_alignbit(w.d3, w.d2, 16);
+    x1 = __builtin_amdgcn_alignbit(w.d4, w.d3, 16);
+    sc = w.d4 >> 16;
+  } else {
+    x0 = w.d0;
+    x1 = w.d1;
+    sc = w.d2 & 0xFFFFu;
+  }
+  const bool bad = scale_flags_set<0>(scale_pair_bad<0>(sc));
+  const uint32_t X = kh ? x1 : x0;
+  uint32_t lo, hi;
+  half_table<0>(kh ? sc >> 8 : sc, bad, fix, lo, hi);
+  uint32_t o[8];
+  expand_half_f16(X, lo, hi, o);
+  a0 = __builtin_bit_cast(v8h, make_uint4(o[0], o[1], o[2], o[3]));
+  a1 = __builtin_bit_cast(v8h, make_uint4(o[4], o[5], o[6], o[7]));
+}
+
+// One stage of activations for one thread: token t / 4, blocks 2 (t % 4)
+// and 2 (t % 4) + 1 of the stage.
+struct ActPair {
+  uint4 q0, q1, q2, q3;
+  float d0, d1;
+};
+
+__device__ __forceinline__ void load_acts(ActPair& a, const int8_t* qrow, const float* drow,
+                                          int kb) {
+  const uint4* src = reinterpret_cast<const uint4*>(qrow + (int64_t)kb * 32);
+  a.q0 = src[0];
+  a.q1 = src[1];
+  a.q2 = src[2];
+  a.q3 = src[3];
+  a.d0 = drow[kb];
+  a.d1 = drow[kb + 1];
+}
+
+__device__ __forceinline__ void store_act_block(uint4 lo_half, uint4 hi_half, float d,
+                                                MoeStage& st, int m, int b) {
+  uint8_t* row = st.ah + m * kMoeActRow + b * 64;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint4 v = h ? hi_half : lo_half;
+    const uint32_t X[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[8];
+    act_half_f16(X, o);
+    // step 0 takes values o[0..3] of both halves, step 1 values o[4..7]
+    *reinterpret_cast<uint4*>(row + h * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(row + 32 + h * 16) = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+  st.ad[b][m] = d;
+}
+
+// Block b of the stage against this wave's A operands: both token tiles
+// (the second only when the tile holds more than 32 slots).
+__device__ __forceinline__ void moe_block(const MoeStage& st, int b, int lane, v8h a0, v8h a1,
+                                          bool two, v16f (&acc)[2]) {
+  const int kh = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (t == 1 && !two) break;
+    const int m = t * 32 + (lane & 31);
+    const uint8_t* row = st.ah + m * kMoeActRow + b * 64 + kh * 16;
+    const v8h b0 = *reinterpret_cast<const v8h*>(row);
+    const v8h b1 = *reinterpret_cast<const v8h*>(row + 32);
+    const float dd = st.ad[b][m];
+    v16f c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, v16f{}, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, c, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = fmaf(dd, c[r], acc[t][r]);
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void moe_gemm_kernel(GemmF16Params p) {
+  __shared__ MoeStage sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kh = lane >> 5;
+  const int N = p.N, K = p.K;
+  const int64_t row_bytes = (int64_t)(K / 32) * 10;
+  const int nb = K / 32;
+  const int nst = nb / kMoeKB;                  // K % 256 == 0
+  const float fix = scale_fix();
+
+  // token tile i runs on XCD i % 8 with all of its row tiles (its gathered
+  // activations stay in that XCD's L2); workgroups past the last tile leave
+  const int x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+  const int i = kXcds * (k / p.n_tiles) + x;
+  if (i >= p.tile_start[p.E]) return;
+  const int e = expert_of_tile(p.tile_start, p.E, i, lane);
+  const int start = p.offsets[e] + (i - p.tile_start[e]) * kMoeTokens;
+  const int rows = min(kMoeTokens, p.offsets[e + 1] - start);
+  const int n0 = (k % p.n_tiles) * kMoeRows;
+  const bool two = rows > 32;                   // uniform
+
+  // this lane's weight row; this thread's activation token and blocks
+  const int n = n0 + wave * 32 + (lane & 31);
+  const uint8_t* wrow = p.w + (int64_t)e * N * row_bytes + (int64_t)(n < N ? n : 0) * row_bytes;
+  const int am = tid >> 2, ab = 2 * (tid & 3);
+  const int token = p.order[start + min(am, rows - 1)] / p.top_k;
+  const int8_t* qrow = p.q + (int64_t)token * K + ab * 32;
+  const float* drow = p.d + (int64_t)token * nb + ab;
+
+  v16f acc[2] = {v16f{}, v16f{}};
+  WPair w0, w1, w2, w3;                         // the stage's four pairs of blocks
+  load_pair(w0, wrow, 0);
+  load_pair(w1, wrow, 2);
+  load_pair(w2, wrow, 4);
+  load_pair(w3, wrow, 6);
+  ActPair ap;
+  load_acts(ap, qrow, drow, 0);
+
+  for (int s = 0; s < nst; ++s) {
+    const int kb_next = min(s + 1, nst - 1) * kMoeKB;   // past the end: re-read
+    __syncthreads();                            // every wave is done with the stage buffer
+    store_act_block(ap.q0, ap.q1, ap.d0, sm, am, ab);
+    store_act_block(ap.q2, ap.q3, ap.d1, sm, am, ab + 1);
+    load_acts(ap, qrow, drow, kb_next);
+    __syncthreads();
+    v8h a0, a1;
+    decode_half<0>(w0, kh, fix, a0, a1);
+    moe_block(sm, 0, lane, a0, a1, two, acc);
+    decode_half<1>(w0, kh, fix, a0, a1);
+    load_pair(w0, wrow, kb_next + 0);
+    moe_block(sm, 1, lane, a0, a1, two, acc);
+    decode_half<0>(w1, kh, fix, a0, a1);
+    moe_block(sm, 2, lane, a0, a1, two, acc);
+    decode_half<1>(w1, kh, fix, a0, a1);
+    load_pair(w1, wrow, kb_next + 2);
+    moe_block(sm, 3, lane, a0, a1, two, acc);
+    decode_half<0>(w2, kh, fix, a0, a1);
+    moe_block(sm, 4, lane, a0, a1, two, acc);
+    decode_half<1>(w2, kh, fix, a0, a1);
+    load_pair(w2, wrow, kb_next + 4);
+    moe_block(sm, 5, lane, a0, a1, two, acc);
+    decode_half<0>(w3, kh, fix, a0, a1);
+    moe_block(sm, 6, lane, a0, a1, two, acc);
+    decode_half<1>(w3, kh, fix, a0, a1);
+    load_pair(w3, wrow, kb_next + 6);
+    moe_block(sm, 7, lane, a0, a1, two, acc);
+  }
+
+  // lane -> token, register r -> row; rows n..n+3 of a register group are
+  // contiguous in y, so whole groups go out as one 16-byte store
+  const bool vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int m = t * 32 + (lane & 31);
+    if (m >= rows) continue;
+    float* yr = p.y + (int64_t)p.order[start + m] * N;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int nn = n0 + wave * 32 + 8 * g + 4 * kh;
+      const v16f& v = acc[t];
+      if (vec && nn + 3 < N) {
+        *reinterpret_cast<float4*>(yr + nn) =
+            make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (nn + q < N) yr[nn + q] = v[4 * g + q];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_f16(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
@@ -377,21 +569,20 @@ hipError_t launch_gemm_f16(const uint8_t* w, int64_t N, int64_t K, const int8_t*
   p.m_tiles = (int)((M + BM - 1) / BM);
   const int n_tiles = (int)((N + BN - 1) / BN);
   p.tiles = p.m_tiles * n_tiles;
-  hipLaunchKernelGGL((gemm_f16_kernel<2, false>), dim3((uint32_t)p.tiles), dim3(256), 0,
+  hipLaunchKernelGGL((gemm_f16_kernel<2>), dim3((uint32_t)p.tiles), dim3(256), 0,
                      stream, p);
   return hipGetLastError();
 }
 
-int moe_gemm_tile_tokens() { return StageF16<1>::BM; }
+int moe_gemm_tile_tokens() { return kMoeTokens; }
 
 // Workgroups of the routed product: every row tile of the most token tiles
 // any routing of S slots over E experts can need (at most one partly filled
 // tile per expert that has slots), rounded up to whole rounds of the XCDs.
 int64_t moe_gemm_max_grid(int64_t E, int64_t N, int64_t S) {
-  constexpr int BM = StageF16<1>::BM;
-  const int64_t max_tiles = (S + BM - 1) / BM + std::min<int64_t>(E, S);
+  const int64_t max_tiles = (S + kMoeTokens - 1) / kMoeTokens + std::min<int64_t>(E, S);
   const int64_t per_xcd = (max_tiles + kXcds - 1) / kXcds;
-  return (int64_t)kXcds * ((N + BN - 1) / BN) * per_xcd;
+  return (int64_t)kXcds * ((N + kMoeRows - 1) / kMoeRows) * per_xcd;
 }
 
 // Routed product over slots already sorted by expert (offsets, tile_start,
@@ -401,15 +592,13 @@ hipError_t launch_moe_gemm_sorted(const uint8_t* w, int64_t E, int64_t N, int64_
                                   const int32_t* order, int64_t S, int64_t top_k,
                                   const int8_t* q, const float* d, float* y,
                                   hipStream_t stream) {
-  constexpr int BM = StageF16<1>::BM;
   GemmF16Params p{};
   p.w = w; p.N = (int)N; p.K = (int)K; p.q = q; p.d = d; p.y = y;
   p.offsets = offsets; p.tile_start = tile_start; p.order = order;
   p.E = (int)E; p.top_k = (int)top_k;
-  p.n_tiles = (int)((N + BN - 1) / BN);
+  p.n_tiles = (int)((N + kMoeRows - 1) / kMoeRows);
   const int64_t grid = moe_gemm_max_grid(E, N, S);
-  hipLaunchKernelGGL((gemm_f16_kernel<1, true>), dim3((uint32_t)grid), dim3(256), 0, stream,
-                     p);
+  hipLaunchKernelGGL(moe_gemm_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
