@@ -45,9 +45,10 @@ KERNEL_SOURCES = ["rfp2_device.h", "gemv_kernel.h", "gemv.hip", "gemv_moe.hip", 
                   "gemm_f16.hip", "moe_sort.hip", "quantize.hip"]
 
 
-def kernel_hash() -> str:
+def kernel_hash(sources=None) -> str:
+    """Hash of the kernel sources (all of them by default)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, "bit_gemv_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -86,16 +87,17 @@ def algorithmic(cfg, one_launch: bool = False) -> dict:
     return {"quant_bytes": quant, "product_bytes": prod, "ops": ops}
 
 
-def traffic_from_profiles(workload: str, khash: str):
+def traffic_from_profiles(workload: str, khash: str = ""):
     """HBM bytes per launch of the product kernel, from the committed counter
-    summary, if it was taken on the current kernel sources."""
+    summary, if it was taken on the current sources of that kernel (the
+    record names the files its hash covers)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_hash") != khash:
+    if not rec or rec.get("kernel_hash") != kernel_hash(rec.get("hash_sources")):
         return None
     return rec.get("hbm_bytes_per_launch")
 
