@@ -284,9 +284,11 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
         y_eager = y.clone()
 
         # The timed loops are replayed from HIP graphs: one graph holds
-        # `per_graph` consecutive steps (weights rotating over the copies), so
-        # the host's launch cost does not set the pace.
-        per_graph = max(1, min(steps, copies, 64))
+        # `per_graph` consecutive steps, so neither the host's launch cost nor
+        # the gap between replays sets the pace.  The weights rotate over the
+        # copies inside the graph: a copy comes back only after >= 1 GiB of
+        # other weights, so every step still reads its weights from HBM.
+        per_graph = max(1, min(steps, 64))
         g_step = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_step, stream=stream):
             for i in range(per_graph):
