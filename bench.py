@@ -148,6 +148,56 @@ def cpu_baseline(cfg, budget_s: float = 12.0) -> dict:
     return out
 
 
+def graph_time_us(launch, steps: int) -> float:
+    """Mean time of launch(i, stream) over back-to-back replays of a HIP graph
+    holding up to 64 consecutive launches (as the products are timed)."""
+    import torch
+    stream = torch.cuda.Stream()
+    per_graph = max(1, min(steps, 64))
+    with torch.cuda.stream(stream):
+        launch(0, stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(per_graph):
+                launch(i, stream)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // per_graph)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / (reps * per_graph)
+        del g
+    return us
+
+
+def measure_ceiling(nbytes: int, steps: int) -> dict:
+    """The read ceiling at a product's byte count: rfp2_read_ceiling (plain
+    coalesced 16-byte loads) over distinct slices of >= 1 GiB, so every read
+    comes from HBM as the products' weights do; and one read of 1 GiB."""
+    import torch
+    import bit_gemv_amd as rf
+    dev = torch.device("cuda:0")
+    nb = max(16, nbytes // 16 * 16)
+    slots = max(2, -(-COLD_BYTES // nb))
+    buf = torch.zeros(slots * nb, dtype=torch.uint8, device=dev)
+    out = torch.empty(rf.READ_CEILING_OUTPUTS, dtype=torch.int32, device=dev)
+    us = graph_time_us(lambda i, st: rf.rfp2_read_ceiling(buf[(i % slots) * nb:], nb, out, st),
+                       steps)
+    big = COLD_BYTES // 16 * 16
+    us_big = graph_time_us(lambda i, st: rf.rfp2_read_ceiling(buf, big, out, st),
+                           min(steps, 64))
+    del buf, out
+    torch.cuda.empty_cache()
+    return {"kernel": "rfp2_read_ceiling", "bytes": nb, "us": us, "GBps": nb / us / 1e3,
+            "GBps_1GiB": big / us_big / 1e3}
+
+
 def measure_quantizer(workload: str, reps: int = 5) -> dict:
     """Weight-quantizer throughput on the workload's matrix: the plain and
     the importance-weighted scale search on the GPU (weights per second,
@@ -360,6 +410,12 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
     roof.update(traffic=traffic_from_profiles(workload, khash), kernel=kernel,
                 kernel_us=kern_ms * 1e3, algorithmic_bytes=alg["product_bytes"],
                 algorithmic_ops=alg["ops"])
+    if roof["bound"] == "hbm":
+        # what a plain read of the same bytes reaches: the product's bandwidth
+        # is reported against it besides the HBM peak
+        ceil = measure_ceiling(alg["product_bytes"], steps)
+        ceil["frac_of_ceiling"] = roof["achieved"] / ceil["GBps"]
+        roof["ceiling"] = ceil
     config = {"workload": workload, "M": M, "N": N, "K": K}
     if cfg["op"] in ("moe", "moe_tokens", "moe_gemm"):
         config.update(experts=cfg["E"], top_k=cfg["top_k"])
@@ -411,7 +467,8 @@ def main(argv=None) -> int:
                           "unit": s["unit"], "ms_per_step": s["ms_per_step"],
                           "roofline": {k: s["roofline"][k] for k in
                                        ("bound", "achieved", "peak", "unit", "frac",
-                                        "kernel", "kernel_us", "traffic")}})
+                                        "kernel", "kernel_us", "traffic", "ceiling")
+                                       if k in s["roofline"]}})
     if secondary:
         out["secondary"] = secondary
     if not args.no_cpu_baseline:

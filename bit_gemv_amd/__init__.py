@@ -42,6 +42,7 @@ _SIGNATURES = {
     "rfp2_moe_gemm_workspace_bytes": ([_c_i64, _c_i64, _c_i64], ctypes.c_size_t),
     "rfp2_moe_gemm": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p,
                        _c_p, _c_p, ctypes.c_size_t, _c_p], ctypes.c_int),
+    "rfp2_read_ceiling": ([_c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
     "rfp2_quant_gemv": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p], ctypes.c_int),
     "rfp2_quant_moe_gemv": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p,
                              _c_p, _c_p, _c_p], ctypes.c_int),
@@ -222,6 +223,18 @@ def rfp2_moe_gemm(w, E: int, N: int, K: int, ids, T: int, top_k: int, q, d, y, e
         _ptr(q, torch.int8, T * K, "q"), _ptr(d, torch.float32, T * _blocks(K), "d"),
         _ptr(y, torch.float32, T * top_k * N, "y"), errp,
         _ptr(workspace, torch.uint8, need, "workspace"), workspace.numel(), _stream(stream)))
+
+
+READ_CEILING_OUTPUTS = 2048
+
+
+def rfp2_read_ceiling(buf, nbytes: int, out, stream=None) -> None:
+    """Measurement helper: read nbytes of buf with plain 16-byte loads."""
+    import torch
+    _check("rfp2_read_ceiling", lib().rfp2_read_ceiling(
+        _ptr(buf, torch.uint8, nbytes, "buf"), nbytes,
+        _ptr(out, torch.int32, min(READ_CEILING_OUTPUTS, -(-nbytes // 4096)), "out"),
+        _stream(stream)))
 
 
 def rfp2_quant_gemv(w, N: int, K: int, a, q, d, y, stream=None) -> None:

@@ -177,6 +177,15 @@ rfp2_status rfp2_moe_gemm(const uint8_t* w, int64_t E, int64_t N, int64_t K,
                                         stream));
 }
 
+rfp2_status rfp2_read_ceiling(const uint8_t* buf, int64_t bytes, uint32_t* out,
+                              hipStream_t stream) {
+  if (!buf || !out) return RFP2_E_NULL;
+  if (bytes < 16 || bytes % 16 != 0) return RFP2_E_SHAPE;
+  if (!aligned(buf, 16) || !aligned(out, 4)) return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(rfp2::launch_read_ceiling(buf, bytes, out, stream));
+}
+
 rfp2_status rfp2_quant_gemv(const uint8_t* w, int64_t N, int64_t K, const float* a,
                             int8_t* q, float* d, float* y, hipStream_t stream) {
   if (!w || !a || !q || !d || !y) return RFP2_E_NULL;
