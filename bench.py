@@ -109,12 +109,18 @@ def cpu_baseline(cfg, budget_s: float = 12.0) -> dict:
     import numpy as np
     import oracle
     import synth
+    blas_lib = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                            if p.get("user_api") == "blas"] or [1])
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        blas_threads = max([p.get("num_threads", 1) for p in blas] or [1])
+        if blas:
+            blas_lib = f"{blas[0].get('internal_api', '?')} {blas[0].get('version', '')}".strip()
     except Exception:
         blas_threads = 1
+    host = (f"host: os.cpu_count()={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}, "
+            f"numpy {np.__version__}, BLAS {blas_lib} with {blas_threads} threads "
+            f"(the unpack/dequantize steps are single-threaded numpy)")
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
     rows = min(N, 256)
     if cfg["op"] == "moe":
@@ -140,7 +146,8 @@ def cpu_baseline(cfg, budget_s: float = 12.0) -> dict:
     sample_ops = 2 * Mb * rows * K
     out = {"cores": int(blas_threads), "kind": "oracle",
            "sample": f"{rows} weight rows x {Mb} token(s) of {cfg['name']}, "
-                     f"{reps} timed repetitions of quantize_acts + ref_gemv (fp64, numpy)"}
+                     f"{reps} timed repetitions of quantize_acts + ref_gemv (fp64, numpy); "
+                     + host}
     if cfg["op"] in ("gemm", "gemm_f16"):
         out.update(value=sample_ops / per / 1e12, unit="TOPS")
     else:
