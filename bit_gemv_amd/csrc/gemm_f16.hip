@@ -411,8 +411,8 @@ __device__ __forceinline__ void decode_half(const WPair& w, int kh, float fix, v
   a1 = __builtin_bit_cast(v8h, make_uint4(o[4], o[5], o[6], o[7]));
 }
 
-// One stage of activations for one thread: token t / 4, blocks 2 (t % 4)
-// and 2 (t % 4) + 1 of the stage.
+// One stage of activations for one thread: token t % 64, blocks 2 (t / 64)
+// and 2 (t / 64) + 1 of the stage.
 struct ActPair {
   uint4 q0, q1, q2, q3;
   float d0, d1;
@@ -491,7 +491,9 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_kernel(GemmF16Params p) {
   // this lane's weight row; this thread's activation token and blocks
   const int n = n0 + wave * 32 + (lane & 31);
   const uint8_t* wrow = p.w + (int64_t)e * N * row_bytes + (int64_t)(n < N ? n : 0) * row_bytes;
-  const int am = tid >> 2, ab = 2 * (tid & 3);
+  // (consecutive lanes take consecutive tokens: their 16-byte LDS stores,
+  // 528 bytes apart, fall on distinct banks)
+  const int am = tid & 63, ab = 2 * (tid >> 6);
   const int token = p.order[start + min(am, rows - 1)] / p.top_k;
   const int8_t* qrow = p.q + (int64_t)token * K + ab * 32;
   const float* drow = p.d + (int64_t)token * nb + ab;
