@@ -115,6 +115,40 @@ def test_moe_gemm_against_oracle_and_dense(T, top_k, K, kind):
     assert np.isnan(y[np.flatnonzero(bad.reshape(-1))]).all()
 
 
+@pytest.mark.parametrize("E,T,top_k,K,N", [(2048, 4096, 2, 256, 130),   # long sort chunks
+                                          (40, 300, 2, 16384, 200)])     # 64 stages of K
+def test_moe_gemm_large_shapes_against_dense(E, T, top_k, K, N):
+    # every routed row bit for bit against rfp2_gemm_f16 of its expert, and
+    # sampled rows against the oracle
+    announce("moe_gemm large", E, T, top_k, K, N)
+    dev = device()
+    rng = np.random.default_rng(E + T + K)
+    ids = rng.integers(0, E, (T, top_k)).astype(np.int32)
+    ids[rng.random((T, top_k)) < 0.3] = 5                  # one crowded expert
+    rb = N * (K // 32) * 10
+    bank = torch.randint(0, 0x28, (E * rb,), dtype=torch.uint8, device=dev)
+    q, d = oracle.quantize_acts(synth.activations(T, K, seed=E))
+    q_g, d_g = to_dev(q), to_dev(d)
+    y_g, err = run_moe_gemm(bank, E, N, K, ids, q_g, d_g)
+    assert err == 0
+    flat = ids.reshape(-1)
+    bank_h = None
+    for e in sorted(set(flat.tolist())):
+        slots = np.flatnonzero(flat == e)
+        toks = slots // top_k
+        dense = dense_rows(bank[e * rb:(e + 1) * rb], N, K, q_g, d_g, T)
+        assert torch.equal(y_g[torch.from_numpy(slots).to(dev)],
+                           dense[torch.from_numpy(toks).to(dev)]), f"expert {e}"
+        if e == 5 or e == int(flat[0]):
+            if bank_h is None:
+                bank_h = host(bank).reshape(E, N, -1)
+            rows = sample_rows(N, 6, seed=e)
+            y = host(y_g)
+            ref = oracle.ref_gemv(bank_h[e][rows], len(rows), K, q[toks], d[toks])
+            absum = oracle.abs_product_sums(bank_h[e][rows], len(rows), K, q[toks], d[toks])
+            assert_within_bound(y[np.ix_(slots, rows)], ref, absum, f"expert {e}")
+
+
 def test_moe_gemm_workspace_and_limits():
     device()
     E, N, K, T, top_k = 4, 64, 256, 10, 2
