@@ -59,8 +59,7 @@ __device__ __forceinline__ void group_product(const uint32_t (&dw)[20],
     }
     const uint32_t sc = dw[o + 2];   // scale pair: bytes 0,1 (even) or 2,3 (odd)
     uint32_t W0[4], W1[4];
-    expand_half(c0, W0);
-    expand_half(c1, W1);
+    expand_block(c0, c1, W0, W1);
     // both scales of the block in one packed fp8 convert.  gfx950 converts
     // OCP E4M3FN, where byte 0x7F is NaN: it poisons the row through the
     // product.  Bytes 0x80..0xFF are caught by their top bits, OR-ed into
@@ -193,7 +192,9 @@ __device__ __forceinline__ void load_acts_and_chunk(const float* abase, uint32_t
 //     |t - k| < 0.49997, k is roundf(fl32(a / d)) (fl32 adds at most 3.9e-6).
 //   * Otherwise (t within 3e-5 of a half-integer), or when d is subnormal,
 //     the lane redoes its values with the IEEE division and roundf.
-// X receives q packed four per dword in natural order; returns d.
+// A receives q packed four per dword in the lane order of the expanded
+// weights (A[i] = q[i], q[4+i], q[8+i], q[12+i]: packing in that order costs
+// the same as packing in natural order and saves the transpose); returns d.
 __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2,
                                                    uint32_t b3) {
   // v_perm: selector bytes 0..3 pick from the second source, 4..7 from the
@@ -203,7 +204,15 @@ __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uin
   return lo | hi;
 }
 
-__device__ __forceinline__ float quantize_half(const v4f (&x)[4], uint32_t (&X)[4]) {
+// max(|x|, |y|, |z|), NaN when any of them is NaN (IEEE 754-2019 maximum;
+// the older three-input max drops a quiet NaN operand).
+__device__ __forceinline__ float maximum3_abs(float x, float y, float z) {
+  float r;
+  asm("v_maximum3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+  return r;
+}
+
+__device__ __forceinline__ float quantize_half(const v4f (&x)[4], uint32_t (&A)[4]) {
   constexpr float kMagic = 12582912.0f;          // 1.5 * 2^23
   float v[16];
 #pragma unroll
@@ -213,13 +222,16 @@ __device__ __forceinline__ float quantize_half(const v4f (&x)[4], uint32_t (&X)[
     v[4 * i + 2] = x[i].z;
     v[4 * i + 3] = x[i].w;
   }
-  // max |a| as the largest magnitude bit pattern: NaN and Inf sort above
-  // every finite value, so the same max decides finiteness
-  uint32_t amb = 0;
+  // max |a| with the NaN-propagating three-input maximum (a NaN anywhere
+  // gives NaN), then as a bit pattern, where NaN and Inf sort above every
+  // finite value, so the same max decides finiteness
+  float am = maximum3_abs(v[0], v[1], v[2]);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) amb = max(amb, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  for (int i = 3; i < 15; i += 2) am = maximum3_abs(am, v[i], v[i + 1]);
+  am = maximum3_abs(am, v[15], v[15]);
+  uint32_t amb = __float_as_uint(am);
   amb = max(amb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amb, 0xB1, 0xF, 0xF, false));
-  X[0] = X[1] = X[2] = X[3] = 0u;
+  A[0] = A[1] = A[2] = A[3] = 0u;
   if (amb >= 0x7F800000u) return __builtin_nanf("");
   const float dv = __fdiv_rn(__uint_as_float(amb), 127.0f);
   if (dv == 0.0f) return dv;
@@ -239,7 +251,7 @@ __device__ __forceinline__ float quantize_half(const v4f (&x)[4], uint32_t (&X)[
       u[i] = __float_as_uint(roundf(__fdiv_rn(v[i], dv)) + kMagic);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) X[i] = pack_low_bytes(u[4 * i], u[4 * i + 1], u[4 * i + 2], u[4 * i + 3]);
+  for (int i = 0; i < 4; ++i) A[i] = pack_low_bytes(u[i], u[4 + i], u[8 + i], u[12 + i]);
   return dv;
 }
 
@@ -381,9 +393,9 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
     // Quantizing form: lane h of the wave takes half h of the wave's slice
     // (ag*16 <= 64 halves; lanes past the end repeat the last one and write
     // nothing), loads its fp32 activations and the weight chunk in one go,
-    // quantizes while the weights stream, and writes the int8 half
-    // (transposed) and the block scale to the same LDS slots the loaded
-    // form uses.  Workgroup 0 also writes q and d out.
+    // quantizes while the weights stream, and writes the int8 half (in the
+    // lane order of the expanded weights) and the block scale to the same
+    // LDS slots the loaded form uses.  Workgroup 0 also writes q and d out.
     const int n_halves = ag * 16;
     const int h = min(lane, n_halves - 1);
     const int lgl = h >> 4, piece = h & 15;
@@ -391,14 +403,14 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
     v4f x[4];
     load_acts_and_chunk(p.a, (uint32_t)((grp * 256 + piece * 16) * 4),
                         wb + (int64_t)(wave << ls) * 80, co, ring_m0, x);
-    uint32_t X[4];
-    const float dv = quantize_half(x, X);
+    uint32_t A[4];
+    const float dv = quantize_half(x, A);
     if (lane < n_halves) {
-      uint32_t A[4];
-      transpose_half(X, A);
       reinterpret_cast<uint4*>(alds)[lgl * kGroupPieces + piece] = make_uint4(A[0], A[1], A[2], A[3]);
       if ((piece & 1) == 0) dlds[lgl * 8 + (piece >> 1)] = dv;
       if (blockIdx.x == 0 && (!MOE || blockIdx.y == 0)) {
+        uint32_t X[4];                 // the transpose is its own inverse
+        transpose_half(A, X);
         reinterpret_cast<uint4*>(p.qo)[grp * 16 + piece] = make_uint4(X[0], X[1], X[2], X[3]);
         if ((piece & 1) == 0) p.dout[grp * 8 + (piece >> 1)] = dv;
       }

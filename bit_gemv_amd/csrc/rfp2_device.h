@@ -34,6 +34,32 @@ __device__ __forceinline__ void expand_half(uint32_t X, uint32_t (&W)[4]) {
   W[3] = __builtin_amdgcn_perm(kLevels, kLevels, (X >> 6) & kLow2);
 }
 
+// Both halves of one block at once: C0, C1 are the two halves' code words.
+// The shifts by 2, 4 and 6 are taken on the 64-bit pair C1:C0, one
+// instruction for both halves (bits of C1 that enter the top of the low
+// word are above every byte's low two bits and are masked off).  The compiler
+// splits a 64-bit shift whose halves are used separately into two 32-bit
+// ones, so the shift is written as asm.
+template <int N>
+__device__ __forceinline__ uint64_t shr64(uint64_t x) {
+  uint64_t r;
+  asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "I"(N), "v"(x));
+  return r;
+}
+__device__ __forceinline__ void expand_block(uint32_t C0, uint32_t C1, uint32_t (&W0)[4],
+                                             uint32_t (&W1)[4]) {
+  const uint64_t C = ((uint64_t)C1 << 32) | C0;
+  W0[0] = __builtin_amdgcn_perm(kLevels, kLevels, C0 & kLow2);
+  W1[0] = __builtin_amdgcn_perm(kLevels, kLevels, C1 & kLow2);
+  const uint64_t S2 = shr64<2>(C), S4 = shr64<4>(C), S6 = shr64<6>(C);
+  W0[1] = __builtin_amdgcn_perm(kLevels, kLevels, (uint32_t)S2 & kLow2);
+  W1[1] = __builtin_amdgcn_perm(kLevels, kLevels, (uint32_t)(S2 >> 32) & kLow2);
+  W0[2] = __builtin_amdgcn_perm(kLevels, kLevels, (uint32_t)S4 & kLow2);
+  W1[2] = __builtin_amdgcn_perm(kLevels, kLevels, (uint32_t)(S4 >> 32) & kLow2);
+  W0[3] = __builtin_amdgcn_perm(kLevels, kLevels, (uint32_t)S6 & kLow2);
+  W1[3] = __builtin_amdgcn_perm(kLevels, kLevels, (uint32_t)(S6 >> 32) & kLow2);
+}
+
 // 4x4 byte transpose of the 16 int8 activations of one half: X[j] holds
 // a[4j..4j+3] in natural order; A[i] = (a[i], a[4+i], a[8+i], a[12+i]), the
 // lane order expand_half produces for the weights.
