@@ -38,51 +38,111 @@ struct Params {
 // Decode one 80-byte group held in registers and accumulate its product with
 // M activation columns.  `act` points at the LDS activations of column 0 for
 // this group and `dact` at its 8 block scales; columns are `act_stride` and
-// `d_stride` dwords apart.
-template <int M>
+// `d_stride` dwords apart.  Up to four columns, a block's activations are
+// read from LDS one block ahead of its products, so that their latency hides
+// behind the previous block's vector work (measured at 16384 x 5120: M = 1,
+// 2, 4 take 2, 5 and 7 % less time); with more columns the extra registers
+// cost more waves per SIMD than the latency they hide (M = 8: 15 % slower),
+// and each block reads its own activations.
+// Block jb of the group against the M columns; acts(m, A0, A1, d) supplies
+// column m's activations (two words of 16 int8) and block scale.
+template <int M, typename Acts>
+__device__ __forceinline__ void block_product(const uint32_t (&dw)[20], int jb, Acts acts,
+                                              float (&acc)[M], uint32_t& bad_lo,
+                                              uint32_t& bad_hi, int ncols) {
+  // block jb occupies bytes 10*jb .. 10*jb+9 of the group
+  const int o = (10 * jb) / 4;
+  uint32_t c0, c1;
+  if ((jb & 1) == 0) {          // starts on a dword: codes dw[o], dw[o+1]
+    c0 = dw[o];
+    c1 = dw[o + 1];
+  } else {                       // starts at byte 2 of dw[o]
+    c0 = __builtin_amdgcn_alignbit(dw[o + 1], dw[o], 16);
+    c1 = __builtin_amdgcn_alignbit(dw[o + 2], dw[o + 1], 16);
+  }
+  const uint32_t sc = dw[o + 2];   // scale pair: bytes 0,1 (even) or 2,3 (odd)
+  uint32_t W0[4], W1[4];
+  expand_block(c0, c1, W0, W1);
+  // both scales of the block in one packed fp8 convert.  gfx950 converts
+  // OCP E4M3FN, where byte 0x7F is NaN: it poisons the row through the
+  // product.  Bytes 0x80..0xFF are caught by their top bits, OR-ed into
+  // bad_* (bits 7/15 for an even block, 23/31 for an odd one).
+  const float2 sp = (jb & 1) ? fp8_pair<true>(sc) : fp8_pair<false>(sc);
+  const float s0 = sp.x, s1 = sp.y;
+  if ((jb & 1) == 0)
+    bad_lo |= sc;
+  else
+    bad_hi |= sc;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    if (m >= ncols) break;                  // (uniform) unused columns of a group
+    uint4 A0, A1;
+    float dm;
+    acts(m, A0, A1, dm);
+    const uint32_t a0[4] = {A0.x, A0.y, A0.z, A0.w};
+    const uint32_t a1[4] = {A1.x, A1.y, A1.z, A1.w};
+    const int32_t S0 = half_dot(W0, a0);
+    const int32_t S1 = half_dot(W1, a1);
+    acc[m] = fmaf(dm, fmaf(s1, (float)S1, s0 * (float)S0), acc[m]);
+  }
+}
+
+// Decode one 80-byte group held in registers and accumulate its product with
+// M activation columns.  `act` points at the LDS activations of column 0 for
+// this group and `dact` at its 8 block scales; columns are `act_stride` and
+// `d_stride` dwords apart.  With AHEAD a block's activations are read from
+// LDS one block ahead of its products, so that their latency hides behind
+// the previous block's vector work (dense product at 16384 x 5120: M = 1, 2,
+// 3, 4 take 2.5, 5.5, 5 and 7 % less time); otherwise each block reads its
+// activations where it uses them.  The extra registers cost waves per SIMD:
+// the dense M = 8 product was 15 % slower with it, the routed-token product
+// (128 experts of 1536 x 4096, top-8) 14 % at T = 2 and 30 % at T = 4.
+template <int M, bool AHEAD>
 __device__ __forceinline__ void group_product(const uint32_t (&dw)[20],
                                               const uint32_t* act, int act_stride,
                                               const float* dact, int d_stride,
                                               float (&acc)[M], uint32_t& bad_lo,
                                               uint32_t& bad_hi, int ncols = M) {
+  auto load = [&](int jb, int m, uint4& A0, uint4& A1, float& dm) {
+    const uint32_t* a = act + m * act_stride + jb * 8;
+    A0 = *reinterpret_cast<const uint4*>(a);
+    A1 = *reinterpret_cast<const uint4*>(a + 4);
+    dm = dact[m * d_stride + jb];
+  };
+  if constexpr (AHEAD) {
+    uint4 nA0[M], nA1[M];
+    float nd[M];
+    auto fetch = [&](int jb) {
 #pragma unroll
-  for (int jb = 0; jb < 8; ++jb) {
-    // block jb occupies bytes 10*jb .. 10*jb+9 of the group
-    const int o = (10 * jb) / 4;
-    uint32_t c0, c1;
-    if ((jb & 1) == 0) {          // starts on a dword: codes dw[o], dw[o+1]
-      c0 = dw[o];
-      c1 = dw[o + 1];
-    } else {                       // starts at byte 2 of dw[o]
-      c0 = __builtin_amdgcn_alignbit(dw[o + 1], dw[o], 16);
-      c1 = __builtin_amdgcn_alignbit(dw[o + 2], dw[o + 1], 16);
-    }
-    const uint32_t sc = dw[o + 2];   // scale pair: bytes 0,1 (even) or 2,3 (odd)
-    uint32_t W0[4], W1[4];
-    expand_block(c0, c1, W0, W1);
-    // both scales of the block in one packed fp8 convert.  gfx950 converts
-    // OCP E4M3FN, where byte 0x7F is NaN: it poisons the row through the
-    // product.  Bytes 0x80..0xFF are caught by their top bits, OR-ed into
-    // bad_* (bits 7/15 for an even block, 23/31 for an odd one).
-    const float2 sp = (jb & 1) ? fp8_pair<true>(sc) : fp8_pair<false>(sc);
-    const float s0 = sp.x, s1 = sp.y;
-    if ((jb & 1) == 0)
-      bad_lo |= sc;
-    else
-      bad_hi |= sc;
+      for (int m = 0; m < M; ++m) {
+        if (m >= ncols) break;
+        load(jb, m, nA0[m], nA1[m], nd[m]);
+      }
+    };
+    fetch(0);
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      if (m >= ncols) break;                  // (uniform) unused columns of a group
-      const uint32_t* a = act + m * act_stride + jb * 8;
-      const uint4 A0 = *reinterpret_cast<const uint4*>(a);
-      const uint4 A1 = *reinterpret_cast<const uint4*>(a + 4);
-      const float dm = dact[m * d_stride + jb];
-      const uint32_t a0[4] = {A0.x, A0.y, A0.z, A0.w};
-      const uint32_t a1[4] = {A1.x, A1.y, A1.z, A1.w};
-      const int32_t S0 = half_dot(W0, a0);
-      const int32_t S1 = half_dot(W1, a1);
-      acc[m] = fmaf(dm, fmaf(s1, (float)S1, s0 * (float)S0), acc[m]);
+    for (int jb = 0; jb < 8; ++jb) {
+      uint4 A0[M], A1[M];
+      float dd[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        A0[m] = nA0[m];
+        A1[m] = nA1[m];
+        dd[m] = nd[m];
+      }
+      if (jb < 7) fetch(jb + 1);
+      block_product<M>(dw, jb, [&](int m, uint4& a0, uint4& a1, float& dm) {
+        a0 = A0[m];
+        a1 = A1[m];
+        dm = dd[m];
+      }, acc, bad_lo, bad_hi, ncols);
     }
+  } else {
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb)
+      block_product<M>(dw, jb, [&](int m, uint4& a0, uint4& a1, float& dm) {
+        load(jb, m, a0, a1, dm);
+      }, acc, bad_lo, bad_hi, ncols);
   }
 }
 
@@ -492,8 +552,9 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
       load_chunk(wb + (int64_t)((((j + JT) * p.wk) + wave) << ls) * 80, co,
                  ring_m0 + 5120 * buf_i);
     const int lgl = (j << ls) + t;
-    group_product<M>(buf, alds + lgl * kGroupDwords, act_stride, dlds + lgl * 8, ag * 8, acc,
-                     bad_lo, bad_hi, ncols);
+    group_product<M, (M <= 4) && (!MOE || M == 1)>(buf, alds + lgl * kGroupDwords, act_stride,
+                                                  dlds + lgl * 8, ag * 8, acc, bad_lo, bad_hi,
+                                                  ncols);
   }
 
   // row sum: xor shuffles over the L lanes of the row, then over the waves
