@@ -232,6 +232,8 @@ rfp2_status rfp2_debug_half_dots(const uint8_t* w, int64_t N, int64_t K,
   if (N < 1 || N > kMaxRows || M < 1 || M > kMaxRows || K < 32 || K % 32 != 0 ||
       K > (int64_t(1) << 30))
     return RFP2_E_SHAPE;
+  // M * N * (K / 32) half-sum pairs are indexed in 64 bits: keep it below 2^40
+  if (N * (K / 32) > (int64_t(1) << 40) / M) return RFP2_E_SHAPE;
   if (!aligned(w, 2) || !aligned(q, 4) || !aligned(sums_out, 4)) return RFP2_E_ALIGN;
   (void)hipGetLastError();
   return from_hip(rfp2::launch_debug_half_dots(w, N, K, q, M, sums_out, stream));

@@ -294,7 +294,8 @@ rfp2_status rfp2_read_ceiling(const uint8_t* buf, int64_t bytes, uint32_t* out,
  *
  * rfp2_debug_half_dots: the int32 sum of each 16-weight half against the int8
  * activations, sums_out [M][N][K/32][2] int32.  Requires N >= 1, M >= 1,
- * K >= 32, K % 32 == 0; w 2-byte aligned, q 4-byte aligned.
+ * K >= 32, K % 32 == 0, M * N * (K/32) <= 2^40; w 2-byte aligned, q 4-byte
+ * aligned.
  */
 rfp2_status rfp2_debug_decode(const uint8_t* w, int64_t N, int64_t K,
                               int8_t* codes_out, float* scales_out,

@@ -62,6 +62,8 @@ def test_gemm_moe_quantize_argument_checks():
     assert L.rfp2_quantize_weights(P, 1, 64, P + 1, None) == rf.RFP2_E_ALIGN
     assert L.rfp2_debug_decode(P, 1, 33, P, P, None) == rf.RFP2_E_SHAPE
     assert L.rfp2_debug_half_dots(P, 1, 64, P, 0, P, None) == rf.RFP2_E_SHAPE
+    # M * N * (K/32) beyond 2^40 half-sum pairs is refused before any launch
+    assert L.rfp2_debug_half_dots(P, 1 << 20, 1 << 20, P, 1 << 20, P, None) == rf.RFP2_E_SHAPE
 
 
 def test_moe_sort_and_moe_gemm_argument_checks():
