@@ -41,6 +41,7 @@
 
 #include "gemv_kernel.h"
 
+#include <atomic>
 #include <cstdlib>
 
 namespace rfp2 {
@@ -142,20 +143,48 @@ size_t lds_bytes(int M, const Geometry& g) {
   return (g.wk * per_wave + (size_t)g.wk * g.rows * M) * 4;
 }
 
+int compute_units() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 }  // namespace
 
+// Each launch reads the whole matrix once, so the M columns should go through
+// as few launches as possible.  Up to seven columns, all of them go in one
+// launch whenever their LDS fits what keeps every workgroup resident in one
+// round (160 KiB over the workgroups per compute unit): at 16384 x 5120 (512
+// workgroups) M = 6 and 7 take 18.6 and 20.7 us in one launch against 22.4
+// and 24.5 us as 5+1 and 6+1 columns.  Otherwise (and always for eight
+// columns: one launch took 33.1 us against 27.3 us for 5+3, whether its
+// workgroups held one or two to a compute unit) launches of as many columns
+// as fit 64 KiB.
 hipError_t launch_gemv(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
                        const float* d, int64_t M, float* y, hipStream_t stream) {
   const Geometry g = geometry(K, M, N);
-  int cols = (int)M;
-  while (cols > 1 && lds_bytes(cols, g) > (size_t)kMaxLdsBytes) --cols;
   const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows));
+  const int64_t cus = compute_units();
+  const int64_t share = ((int64_t)grid.x + cus - 1) / cus;
+  const size_t one_round = (size_t)kMaxLdsBytesPerBlock / share;
+  size_t cap = kMaxLdsBytes;
+  if (M <= 7 && lds_bytes((int)M, g) <= one_round) cap = std::max(cap, one_round);
+  int cols = (int)M;
+  while (cols > 1 && lds_bytes(cols, g) > cap) --cols;
   for (int64_t m0 = 0; m0 < M; m0 += cols) {
     const int mc = (int)std::min<int64_t>(cols, M - m0);
+    const size_t lds = lds_bytes(mc, g);
     Params p{w, (int)N, (int)K, q + m0 * K, d + m0 * (K / 32), y + m0 * N,
              g.lshift, g.wk, g.J, nullptr, 0, nullptr, 1, 0, nullptr, nullptr, nullptr};
-    hipLaunchKernelGGL(pick_kernel(mc, g.jt), grid, dim3(64 * g.wk), lds_bytes(mc, g),
-                       stream, p);
+    hipLaunchKernelGGL(pick_kernel(mc, g.jt), grid, dim3(64 * g.wk), lds, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
