@@ -113,3 +113,20 @@ def test_gemv_full_size_sampled_rows(name):
     assert_within_bound(y[:, rows], oracle.ref_gemv(packed_rows, len(rows), K, q, d),
                         oracle.abs_product_sums(packed_rows, len(rows), K, q, d), name)
     assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("M", [6, 7, 8])
+def test_gemv_many_columns_large_matrix(M):
+    # 16384 x 5120 with 6 and 7 columns runs as one launch whose workgroups
+    # take more than 64 KiB of LDS each; 8 columns as launches of 5 and 3:
+    # sampled rows of every column against the oracle
+    N, K = 16384, 5120
+    announce("gemv many columns", N, K, M)
+    packed = random_blocks(N, K, seed=M, scale_lo=0x00, scale_hi=0x30)
+    q, d = oracle.quantize_acts(synth.activations(M, K, seed=40 + M))
+    y = run_gemv(packed, N, K, q, d)
+    rows = sample_rows(N, 48, seed=M)
+    assert_within_bound(y[:, rows], oracle.ref_gemv(packed[rows], len(rows), K, q, d),
+                        oracle.abs_product_sums(packed[rows], len(rows), K, q, d),
+                        f"gemv {N}x{K} M={M}")
+    assert np.isfinite(y).all()
