@@ -3,9 +3,12 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the path over one batch of synthetic input that is
-already resident in HBM: int8 quantization of the fp32 activations
-(rfp2_quantize_acts) followed by the product against ROCmFP2 weights
-(rfp2_gemv, rfp2_moe_gemv or rfp2_gemm, by workload).  The weights are
+already resident in HBM: int8 quantization of the fp32 activations and the
+product against ROCmFP2 weights.  For one token that is the single
+quantizing launch (rfp2_quant_gemv / rfp2_quant_moe_gemv; --two-launch
+splits it); otherwise rfp2_quantize_acts followed by the product
+(rfp2_gemv, rfp2_moe_gemv_tokens, rfp2_gemm, rfp2_gemm_f16, or
+rfp2_moe_sort + the grouped routed GEMM, by workload).  The weights are
 quantized on the GPU (rfp2_quantize_weights) before timing, and the step
 rotates over enough distinct copies of them (>= 1 GiB in all) that every
 step reads its weights from HBM rather than from the 256 MB last-level cache.
