@@ -256,14 +256,24 @@ hipError_t launch_moe_gemv_tokens(const uint8_t* w, int64_t E, int64_t N, int64_
 
 // One token: quantize the activations inside the product kernel when every
 // wave's slice is at most 64 halves (J*L <= 4, which the one-column
-// geometry gives for K up to 8192 and beyond for most K), else the separate
-// quantization kernel followed by the product.  q and d are written either way.
-bool quant_fused(const Geometry& g) { return (g.J << g.lshift) <= 4 && g.jt == 1; }
+// geometry gives for K up to 8192 and beyond for most K) and the call reads
+// at most 128 MiB of weights, else the separate quantization kernel followed
+// by the product.  q and d are written either way.  Every wave of the fused
+// kernel quantizes its own slice (about a fifth of its vector work), which
+// pays for the second launch it saves only while the launch is a large part
+// of the call: one-token steps at K = 5120 took 8.0 / 14.7 / 24.0 / 33.7 /
+// 46.0 us fused against 9.9 / 15.3 / 23.9 / 33.3 / 43.0 us as two launches
+// at 25, 50, 100, 150 and 200 MiB of weights.
+constexpr int64_t kMaxFusedWeightBytes = int64_t(128) << 20;
+
+bool quant_fused(const Geometry& g, int64_t weight_bytes) {
+  return (g.J << g.lshift) <= 4 && g.jt == 1 && weight_bytes <= kMaxFusedWeightBytes;
+}
 
 hipError_t launch_quant_gemv(const uint8_t* w, int64_t N, int64_t K, const float* a,
                              int8_t* q, float* d, float* y, hipStream_t stream) {
   const Geometry g = geometry(K, 1, N);
-  if (!quant_fused(g)) {
+  if (!quant_fused(g, N * (K / 32) * 10)) {
     const hipError_t e = launch_quantize_acts(a, 1, K, q, d, stream);
     if (e != hipSuccess) return e;
     return launch_gemv(w, N, K, q, d, 1, y, stream);
@@ -281,7 +291,7 @@ hipError_t launch_quant_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t
                                  int8_t* q, float* d, float* y, int32_t* err,
                                  hipStream_t stream) {
   const Geometry g = geometry(K, 1, N * top_k);
-  if (!quant_fused(g)) {
+  if (!quant_fused(g, top_k * N * (K / 32) * 10)) {
     const hipError_t e = launch_quantize_acts(a, 1, K, q, d, stream);
     if (e != hipSuccess) return e;
     return launch_moe_gemv(w, E, N, K, ids, top_k, q, d, y, err, stream);

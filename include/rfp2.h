@@ -245,7 +245,8 @@ rfp2_status rfp2_moe_gemm(const uint8_t* w, int64_t E, int64_t N, int64_t K,
  * exactly as rfp2_quantize_acts does, writing q and d, and computes
  * y = W * a as rfp2_gemv does from that q and d ("03 · Runtime": the int8
  * activation operand, its scale, then the product), in a single kernel
- * launch for most K: each wave quantizes the activations it needs while its
+ * launch for most K and up to 128 MiB of weights (beyond, the two launches
+ * are faster): each wave quantizes the activations it needs while its
  * weights stream in.  y, q and d are bit-identical to rfp2_quantize_acts
  * followed by rfp2_gemv with M = 1.
  *   w [N][K/32][10] bytes, 16-byte aligned.   a [K] fp32, 16-byte aligned.

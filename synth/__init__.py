@@ -37,6 +37,11 @@ WORKLOADS = {
                             wseed=0),
     "gemv_16384x5120_m4": dict(op="gemv", M=4, N=16384, K=5120, sigma=0.015,
                                wseed=0),
+    # the same shape of row eight times taller (200 MiB of weights): large
+    # enough that the launch is small against the transfer; context for the
+    # 25 MiB figure, not one of the measured configurations
+    "gemv_131072x5120": dict(op="gemv", M=1, N=131072, K=5120, sigma=0.015,
+                             wseed=0),
     # prompt-batch GEMM (int8 matrix cores; the same product on fp16 ones)
     "gemm_512x14336x4096": dict(op="gemm", M=512, N=14336, K=4096, sigma=0.02,
                                 wseed=0),

@@ -174,3 +174,48 @@ def test_quant_gemv_graph_replays_match_eager():
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(y, y_eager)
+
+
+@pytest.mark.parametrize("N", [83886, 83887])
+def test_quant_gemv_either_side_of_the_two_launch_size(N):
+    # 128 MiB of weights is the largest one-token call done as one quantizing
+    # launch (83886 rows of K = 5120, 1600 bytes each, are just under it,
+    # 83887 just over): on
+    # both sides q, d and y equal the two-call sequence bit for bit, and q, d
+    # the oracle's quantization
+    K = 5120
+    announce("quant_gemv size switch", N, K)
+    packed = random_blocks(N, K, seed=N, scale_hi=0x28)
+    a = synth.activations(1, K, seed=9)[0]
+    (y1, q1, d1), (y2, q2, d2) = run_both(packed, N, K, a)
+    q, d = oracle.quantize_acts(a[None, :])
+    assert np.array_equal(q1, q[0]) and np.array_equal(d1.view(np.uint32), d[0].view(np.uint32))
+    assert np.array_equal(q1, q2) and np.array_equal(d1.view(np.uint32), d2.view(np.uint32))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def test_quant_moe_gemv_above_the_two_launch_size():
+    # 8 routed experts of 16384 x 1024 are 8 * 16384 * 320 = 40 MiB; 7 of
+    # 65536 x 1024 = 140 MiB goes as two launches: both match the two calls
+    announce("quant_moe_gemv size switch")
+    K = 1024
+    a = to_dev(synth.activations(1, K, seed=6)[0])
+    for E, N, ids in ((8, 16384, [3, 1, 7, 0, 2, 6, 5, 4]), (7, 65536, [6, 0, 3, 1, 5, 2, 4])):
+        top_k = len(ids)
+        bank = np.stack([random_blocks(N, K, seed=e, scale_hi=0x28) for e in range(E)])
+        w = to_dev(bank.reshape(-1))
+        ids_g = to_dev(np.array(ids, np.int32))
+        out = []
+        for fused in (True, False):
+            q, d = empty(K, torch.int8), empty(K // 32, torch.float32)
+            y = empty((top_k, N), torch.float32)
+            if fused:
+                rf.rfp2_quant_moe_gemv(w, E, N, K, ids_g, top_k, a, q, d, y)
+            else:
+                rf.rfp2_quantize_acts(a, 1, K, q, d)
+                rf.rfp2_moe_gemv(w, E, N, K, ids_g, top_k, q, d, y)
+            out.append((host(y), host(q), host(d)))
+        (y1, q1, d1), (y2, q2, d2) = out
+        assert np.array_equal(q1, q2) and np.array_equal(d1.view(np.uint32), d2.view(np.uint32))
+        assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), (E, N)
+        del w
