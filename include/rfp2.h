@@ -24,7 +24,8 @@
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is a DEVICE pointer owned by the caller (the library
- *     allocates nothing, frees nothing and keeps no state between calls).
+ *     allocates nothing, frees nothing and keeps no state between calls
+ *     beyond a per-device cache of the GPU's compute-unit count).
  *   - Inputs are never written.  Outputs are overwritten, not accumulated.
  *   - Every call only enqueues work on `stream` (0 = the null stream) and
  *     returns; nothing is synchronised.  Calls are thread-safe.
