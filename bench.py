@@ -20,7 +20,10 @@ throughput (algorithmic bytes of the step / wall time of the step for GEMV
 workloads, 2*M*N*K / step time for the GEMM workload).  `roofline` describes
 the product kernel alone: HIP events on the bench stream around graph
 replays of back-to-back launches of that kernel (so the average includes the
-gap between consecutive kernels).
+gap between consecutive kernels).  For the HBM-bound products it also
+carries `cold_isolated`: 100 single launches, each after a cache flush,
+median and p10 / p90 (see isolated_cold_us), with the plain read timed the
+same way in `ceiling`.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -186,10 +189,47 @@ def graph_time_us(launch, steps: int) -> float:
     return us
 
 
-def measure_ceiling(nbytes: int, steps: int) -> dict:
+def isolated_cold_us(launch, stream, launches: int = 100) -> dict:
+    """One call at a time from cold caches: before each launch a 1 GiB
+    buffer is read and written (torch's in-place add) and then a second
+    1 GiB buffer is only read (torch's max), so the caches end up full of
+    clean lines of neither the weights nor the inputs; HIP events on the same
+    stream bracket the single launch (dispatch included).  The read-only
+    pass matters: lines the add leaves dirty are written back while the timed
+    launch evicts them, which adds the flush's own write traffic to the
+    launch (about 4 us at 26 MB of weights).  Median, p10 and p90 over
+    `launches` launches."""
+    import torch
+    dev = torch.device("cuda:0")
+    rw = torch.zeros(COLD_BYTES, dtype=torch.uint8, device=dev)
+    ro = torch.zeros(COLD_BYTES // 4, dtype=torch.int32, device=dev)
+    times = []
+    with torch.cuda.stream(stream):
+        for _ in range(launches):
+            rw.add_(1)
+            ro.max()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch(stream)
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+    del rw, ro
+    times.sort()
+    n = len(times)
+    return {"median_us": times[n // 2], "p10_us": times[n // 10], "p90_us": times[(9 * n) // 10],
+            "launches": n,
+            "note": "each launch alone after a 1 GiB read-write and a 1 GiB read-only flush; "
+                    "HIP events around the one launch, dispatch included"}
+
+
+def measure_ceiling(nbytes: int, steps: int, isolated: bool = False) -> dict:
     """The read ceiling at a product's byte count: rfp2_read_ceiling (plain
     coalesced 16-byte loads) over distinct slices of >= 1 GiB, so every read
-    comes from HBM as the products' weights do; and one read of 1 GiB."""
+    comes from HBM as the products' weights do; and one read of 1 GiB.  With
+    `isolated`, also the median of single launches timed as isolated_cold_us
+    times the products."""
     import torch
     import bit_gemv_amd as rf
     dev = torch.device("cuda:0")
@@ -202,10 +242,17 @@ def measure_ceiling(nbytes: int, steps: int) -> dict:
     big = COLD_BYTES // 16 * 16
     us_big = graph_time_us(lambda i, st: rf.rfp2_read_ceiling(buf, big, out, st),
                            min(steps, 64))
+    iso = None
+    if isolated:
+        iso = isolated_cold_us(lambda st: rf.rfp2_read_ceiling(buf, nb, out, st),
+                               torch.cuda.Stream())["median_us"]
     del buf, out
     torch.cuda.empty_cache()
-    return {"kernel": "rfp2_read_ceiling", "bytes": nb, "us": us, "GBps": nb / us / 1e3,
-            "GBps_1GiB": big / us_big / 1e3}
+    res = {"kernel": "rfp2_read_ceiling", "bytes": nb, "us": us, "GBps": nb / us / 1e3,
+           "GBps_1GiB": big / us_big / 1e3}
+    if iso is not None:
+        res["isolated_median_us"] = iso
+    return res
 
 
 def measure_quantizer(workload: str, reps: int = 5) -> dict:
@@ -394,8 +441,10 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
         # context only: the same weights every launch, so they stay in the
         # caches (the last-level cache holds 256 MB) -- not an HBM figure
         warm_us = None
+        isolated = None
         if cfg["op"] not in ("gemm", "gemm_f16", "moe_gemm"):
             warm_us = graph_time_us(lambda i, st: product(0, st), steps)
+            isolated = isolated_cold_us(lambda st: product(0, st), stream)
         del g_step, g_prod, bank, master
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -428,11 +477,16 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
     if warm_us is not None:
         roof["warm"] = {"kernel_us": warm_us, "GBps": alg["product_bytes"] / warm_us / 1e3,
                         "note": "same weights every launch: cache-resident, not HBM"}
+    if isolated is not None:
+        isolated["GBps"] = alg["product_bytes"] / isolated["median_us"] / 1e3
+        roof["cold_isolated"] = isolated
     if roof["bound"] == "hbm":
         # what a plain read of the same bytes reaches: the product's bandwidth
         # is reported against it besides the HBM peak
-        ceil = measure_ceiling(alg["product_bytes"], steps)
+        ceil = measure_ceiling(alg["product_bytes"], steps, isolated is not None)
         ceil["frac_of_ceiling"] = roof["achieved"] / ceil["GBps"]
+        if isolated is not None:
+            isolated["frac_of_ceiling"] = ceil["isolated_median_us"] / isolated["median_us"]
         roof["ceiling"] = ceil
     config = {"workload": workload, "M": M, "N": N, "K": K}
     if cfg["op"] in ("moe", "moe_tokens", "moe_gemm"):
@@ -485,7 +539,8 @@ def main(argv=None) -> int:
                           "unit": s["unit"], "ms_per_step": s["ms_per_step"],
                           "roofline": {k: s["roofline"][k] for k in
                                        ("bound", "achieved", "peak", "unit", "frac",
-                                        "kernel", "kernel_us", "traffic", "ceiling", "warm")
+                                        "kernel", "kernel_us", "traffic", "ceiling", "warm",
+                                        "cold_isolated")
                                        if k in s["roofline"]}})
     if secondary:
         out["secondary"] = secondary
