@@ -266,7 +266,7 @@ def measure_quantizer(workload: str, reps: int = 5) -> dict:
     import oracle
     import synth
 
-    cfg = synth.WORKLOADS[workload]
+    cfg = synth.workload(workload)
     N, K = cfg["N"], cfg["K"]
     dev = torch.device("cuda:0")
     W = synth.weights(N, K, cfg["sigma"], seed=cfg["wseed"])
@@ -308,7 +308,7 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
     import bit_gemv_amd as rf
     import synth
 
-    cfg = dict(synth.WORKLOADS[workload], name=workload)
+    cfg = dict(synth.workload(workload), name=workload)
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)

@@ -97,7 +97,8 @@ struct Geometry {
 //     hides latency.
 constexpr int64_t kMinWorkgroupsForJ2 = 512;
 
-Geometry pick_geometry(int64_t K, int j_target) {
+// max_ag: the most groups a wave may cover (J * L), for forms that need it
+Geometry pick_geometry(int64_t K, int j_target, int max_ag = 1 << 30) {
   static constexpr int kWaveRank[kMaxWaves + 1] = {99, 7, 4, 2, 0, 1, 3, 6, 5};
   const int G = (int)(K / 256);
   Geometry best{};
@@ -108,6 +109,7 @@ Geometry pick_geometry(int64_t K, int j_target) {
     for (int wk = 1; wk <= kMaxWaves; ++wk) {
       if ((G / L) % wk) continue;
       const int J = G / L / wk;
+      if ((J << ls) > max_ag) continue;
       // smaller is better: distance from the target J (ties: fewer groups),
       // then the wave-count rank, then fewer lanes per row (more rows)
       const int64_t key = ((int64_t)std::abs(J - j_target) << 32) |
@@ -255,25 +257,40 @@ hipError_t launch_moe_gemv_tokens(const uint8_t* w, int64_t E, int64_t N, int64_
 }
 
 // One token: quantize the activations inside the product kernel when every
-// wave's slice is at most 64 halves (J*L <= 4, which the one-column
-// geometry gives for K up to 8192 and beyond for most K) and the call reads
-// at most 128 MiB of weights, else the separate quantization kernel followed
-// by the product.  q and d are written either way.  Every wave of the fused
-// kernel quantizes its own slice (about a fifth of its vector work), which
-// pays for the second launch it saves only while the launch is a large part
-// of the call: one-token steps at K = 5120 took 8.0 / 14.7 / 24.0 / 33.7 /
-// 46.0 us fused against 9.9 / 15.3 / 23.9 / 33.3 / 43.0 us as two launches
-// at 25, 50, 100, 150 and 200 MiB of weights.
+// wave's slice is at most 64 halves (J*L <= 4 groups: one half per lane) and
+// the call reads at most 128 MiB of weights, else the separate quantization
+// kernel followed by the product.  q and d are written either way.  Every
+// wave of the fused kernel quantizes its own slice (about a fifth of its
+// vector work), which pays for the second launch it saves only while the
+// launch is a large part of the call: one-token steps at K = 5120 took 8.0 /
+// 14.7 / 24.0 / 33.7 / 46.0 us fused against 9.9 / 15.3 / 23.9 / 33.3 /
+// 43.0 us as two launches at 25, 50, 100, 150 and 200 MiB of weights.
+// Where the one-column geometry gives the waves wider slices (K = 6144 and
+// 8192: 8 groups on 3 or 4 waves), the fused launch takes the best geometry
+// with at most 4 groups per wave instead (6 or 8 waves) up to 64 MiB: at
+// K = 8192 and 5, 10, 20, 40, 60 MiB of weights 4.8 / 5.2 / 7.5 / 12.0 /
+// 17.6 us against 6.4 / 7.5 / 9.0 / 13.6 / 17.6 us as two launches, within
+// 2 % either way from 50 to 80 MiB.
 constexpr int64_t kMaxFusedWeightBytes = int64_t(128) << 20;
+constexpr int64_t kMaxFusedOwnGeometryBytes = int64_t(64) << 20;
+constexpr int kMaxFusedGroups = 4;
 
-bool quant_fused(const Geometry& g, int64_t weight_bytes) {
-  return (g.J << g.lshift) <= 4 && g.jt == 1 && weight_bytes <= kMaxFusedWeightBytes;
+// True (and g set) when the one-token call is one quantizing launch.
+bool quant_geometry(int64_t K, int64_t rows_total, int64_t weight_bytes, Geometry& g) {
+  g = geometry(K, 1, rows_total);
+  if (g.jt != 1) return false;
+  if ((g.J << g.lshift) <= kMaxFusedGroups) return weight_bytes <= kMaxFusedWeightBytes;
+  if (weight_bytes > kMaxFusedOwnGeometryBytes) return false;
+  const Geometry f = pick_geometry(K, 1, kMaxFusedGroups);
+  if (f.wk == 0) return false;            // no split gives every wave <= 4 groups
+  g = f;
+  return true;
 }
 
 hipError_t launch_quant_gemv(const uint8_t* w, int64_t N, int64_t K, const float* a,
                              int8_t* q, float* d, float* y, hipStream_t stream) {
-  const Geometry g = geometry(K, 1, N);
-  if (!quant_fused(g, N * (K / 32) * 10)) {
+  Geometry g;
+  if (!quant_geometry(K, N, N * (K / 32) * 10, g)) {
     const hipError_t e = launch_quantize_acts(a, 1, K, q, d, stream);
     if (e != hipSuccess) return e;
     return launch_gemv(w, N, K, q, d, 1, y, stream);
@@ -290,8 +307,8 @@ hipError_t launch_quant_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t
                                  const int32_t* ids, int64_t top_k, const float* a,
                                  int8_t* q, float* d, float* y, int32_t* err,
                                  hipStream_t stream) {
-  const Geometry g = geometry(K, 1, N * top_k);
-  if (!quant_fused(g, top_k * N * (K / 32) * 10)) {
+  Geometry g;
+  if (!quant_geometry(K, N * top_k, top_k * N * (K / 32) * 10, g)) {
     const hipError_t e = launch_quantize_acts(a, 1, K, q, d, stream);
     if (e != hipSuccess) return e;
     return launch_moe_gemv(w, E, N, K, ids, top_k, q, d, y, err, stream);

@@ -248,8 +248,10 @@ rfp2_status rfp2_moe_gemm(const uint8_t* w, int64_t E, int64_t N, int64_t K,
  * activation operand, its scale, then the product), in a single kernel
  * launch for most K and up to 128 MiB of weights (beyond, the two launches
  * are faster): each wave quantizes the activations it needs while its
- * weights stream in.  y, q and d are bit-identical to rfp2_quantize_acts
- * followed by rfp2_gemv with M = 1.
+ * weights stream in.  q and d are bit-identical to rfp2_quantize_acts, and y
+ * to rfp2_gemv with M = 1 on them, except for K = 6144 and 8192 up to 64 MiB
+ * of weights: there the single launch spreads K over more waves than
+ * rfp2_gemv does, so y sums in another order (same fp32 bound).
  *   w [N][K/32][10] bytes, 16-byte aligned.   a [K] fp32, 16-byte aligned.
  *   q [K] int8, 16-byte aligned (written).     d [K/32] fp32, 4-byte aligned
  *   (written).                                 y [N] fp32, 4-byte aligned.
@@ -263,8 +265,8 @@ rfp2_status rfp2_quant_gemv(const uint8_t* w, int64_t N, int64_t K, const float*
  * token given in fp32, with the activation quantization of
  * rfp2_quantize_acts done inside the product launch (as rfp2_quant_gemv).
  * w, ids, y, err and the limits as rfp2_moe_gemv; a, q, d as
- * rfp2_quant_gemv.  y, q and d are bit-identical to rfp2_quantize_acts
- * followed by rfp2_moe_gemv.
+ * rfp2_quant_gemv.  q and d are bit-identical to rfp2_quantize_acts, and y
+ * to rfp2_moe_gemv on them, with the same exception as rfp2_quant_gemv.
  */
 rfp2_status rfp2_quant_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t K,
                                 const int32_t* ids, int64_t top_k, const float* a,

@@ -49,6 +49,23 @@ WORKLOADS = {
                                     sigma=0.02, wseed=0),
 }
 
+GENERIC_GEMV_SIGMA = 0.015
+
+
+def workload(name: str) -> dict:
+    """A named workload, or a dense GEMV of any shape named gemv_<N>x<K> (one
+    token) or gemv_<N>x<K>_m<M> (M tokens), drawn like the large-layer GEMV:
+    weights N(0, 0.015) with outliers, seed 0."""
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    import re
+    m = re.fullmatch(r"gemv_(\d+)x(\d+)(?:_m(\d+))?", name)
+    if m is None:
+        raise KeyError(f"unknown workload {name!r}")
+    return dict(op="gemv", M=int(m.group(3) or 1), N=int(m.group(1)), K=int(m.group(2)),
+                sigma=GENERIC_GEMV_SIGMA, wseed=0)
+
+
 ACT_SEED = 1
 ROUTE_SEED = 2
 OUTLIER_FRACTION = 0.001

@@ -54,3 +54,17 @@ def test_one_launch_adds_the_fp32_activations_and_the_written_q_d():
     # weights and y, fp32 a read, q and d written
     assert one["product_bytes"] == 26_214_400 + 65_536 + 4 * 5120 + 5120 + 4 * 160
     assert one["quant_bytes"] == 0
+
+
+def test_any_dense_gemv_shape_is_a_workload():
+    import pytest
+    assert synth.workload("gemv_16384x5120") is synth.WORKLOADS["gemv_16384x5120"]
+    cfg = synth.workload("gemv_8192x4096")
+    assert (cfg["op"], cfg["M"], cfg["N"], cfg["K"]) == ("gemv", 1, 8192, 4096)
+    assert synth.workload("gemv_8192x4096_m4")["M"] == 4
+    # 8192 rows of 4096: 8192 * 128 blocks * 10 B + q + d + y
+    b = bench.algorithmic(dict(cfg, name="gemv_8192x4096"), one_launch=False)
+    assert b["product_bytes"] == 10_485_760 + 4_096 + 512 + 32_768
+    for bad in ("gemm_8x8", "gemv_8192", "gemv_8x8_x2"):
+        with pytest.raises(KeyError):
+            synth.workload(bad)

@@ -37,12 +37,12 @@ def test_gemv_512x2048_full_oracle_weights():
 
 
 # (N, K, M): ragged row counts, every lanes-per-row geometry (K/256 = 1, 3, 5,
-# 8, 10, 16, 20, 28, 64, 128 groups), 1..8 columns and column chunking (the
+# 8, 10, 16, 20, 28, 56, 64, 128 groups), 1..8 columns and column chunking (the
 # largest K with eight columns runs as eight one-column launches).
 SHAPES = [
     (1, 256, 1), (300, 256, 1), (257, 768, 3), (1000, 1280, 2), (123, 2560, 5),
     (96, 4096, 8), (200, 5120, 4), (130, 7168, 7), (64, 16384, 1), (37, 32768, 1),
-    (70, 16384, 8), (513, 2048, 6), (45, 32768, 8),
+    (70, 16384, 8), (513, 2048, 6), (45, 32768, 8), (50, 14336, 1),
 ]
 
 
