@@ -257,9 +257,10 @@ hipError_t launch_moe_gemv_tokens(const uint8_t* w, int64_t E, int64_t N, int64_
 }
 
 // One token: quantize the activations inside the product kernel when every
-// wave's slice is at most 64 halves (J*L <= 4 groups: one half per lane) and
-// the call reads at most 128 MiB of weights, else the separate quantization
-// kernel followed by the product.  q and d are written either way.  Every
+// wave's slice is at most 4 groups (64 halves, one per lane; J*L <= 4) and
+// the call reads at most 128 MiB of weights, or in the cases below, else the
+// separate quantization kernel followed by the product.  q and d are
+// written either way.  Every
 // wave of the fused kernel quantizes its own slice (about a fifth of its
 // vector work), which pays for the second launch it saves only while the
 // launch is a large part of the call: one-token steps at K = 5120 took 8.0 /
@@ -270,27 +271,45 @@ hipError_t launch_moe_gemv_tokens(const uint8_t* w, int64_t E, int64_t N, int64_
 // with at most 4 groups per wave instead (6 or 8 waves) up to 64 MiB: at
 // K = 8192 and 5, 10, 20, 40, 60 MiB of weights 4.8 / 5.2 / 7.5 / 12.0 /
 // 17.6 us against 6.4 / 7.5 / 9.0 / 13.6 / 17.6 us as two launches, within
-// 2 % either way from 50 to 80 MiB.
+// 2 % either way from 50 to 80 MiB.  Wider still, each lane quantizes two
+// halves (8 groups per wave): with the one-column geometry where it gives 8
+// groups (K = 10240 on 5 waves, 14336 on 7) up to 24 MiB (K = 14336 at 8.8 /
+// 17.5 / 35 / 61 MiB: 6.1 / 7.9 / 14.3 / 20.6 us against 7.6 / 9.1 / 14.0 /
+// 20.3 us), and with the best geometry of at most 8 groups where the
+// one-column one gives 16 (K = 12288 on 6 waves, 16384 on 8) up to 48 MiB
+// (K = 16384 at 20 / 40 MiB: 8.1 / 14.0 us against 10.7 / 15.6 us).
 constexpr int64_t kMaxFusedWeightBytes = int64_t(128) << 20;
 constexpr int64_t kMaxFusedOwnGeometryBytes = int64_t(64) << 20;
-constexpr int kMaxFusedGroups = 4;
+constexpr int64_t kMaxFusedTwoHalvesBytes = int64_t(24) << 20;
+constexpr int64_t kMaxFusedTwoHalvesOwnGeometryBytes = int64_t(48) << 20;
+constexpr int kMaxFusedGroups = 4;        // one half per lane
+constexpr int kMaxFusedGroups2 = 8;       // two halves per lane
 
-// True (and g set) when the one-token call is one quantizing launch.
-bool quant_geometry(int64_t K, int64_t rows_total, int64_t weight_bytes, Geometry& g) {
+// Halves per lane of the one quantizing launch for a one-token call (g set),
+// or 0 when the call runs the two kernels.
+int quant_geometry(int64_t K, int64_t rows_total, int64_t weight_bytes, Geometry& g) {
   g = geometry(K, 1, rows_total);
-  if (g.jt != 1) return false;
-  if ((g.J << g.lshift) <= kMaxFusedGroups) return weight_bytes <= kMaxFusedWeightBytes;
-  if (weight_bytes > kMaxFusedOwnGeometryBytes) return false;
-  const Geometry f = pick_geometry(K, 1, kMaxFusedGroups);
-  if (f.wk == 0) return false;            // no split gives every wave <= 4 groups
+  if (g.jt != 1) return 0;
+  const int ag = g.J << g.lshift;
+  if (ag <= kMaxFusedGroups) return weight_bytes <= kMaxFusedWeightBytes ? 1 : 0;
+  Geometry f = pick_geometry(K, 1, kMaxFusedGroups);
+  if (f.wk > 0) {
+    if (weight_bytes > kMaxFusedOwnGeometryBytes) return 0;
+    g = f;
+    return 1;
+  }
+  if (ag <= kMaxFusedGroups2) return weight_bytes <= kMaxFusedTwoHalvesBytes ? 2 : 0;
+  f = pick_geometry(K, 1, kMaxFusedGroups2);
+  if (f.wk == 0 || weight_bytes > kMaxFusedTwoHalvesOwnGeometryBytes) return 0;
   g = f;
-  return true;
+  return 2;
 }
 
 hipError_t launch_quant_gemv(const uint8_t* w, int64_t N, int64_t K, const float* a,
                              int8_t* q, float* d, float* y, hipStream_t stream) {
   Geometry g;
-  if (!quant_geometry(K, N, N * (K / 32) * 10, g)) {
+  const int qh = quant_geometry(K, N, N * (K / 32) * 10, g);
+  if (qh == 0) {
     const hipError_t e = launch_quantize_acts(a, 1, K, q, d, stream);
     if (e != hipSuccess) return e;
     return launch_gemv(w, N, K, q, d, 1, y, stream);
@@ -298,8 +317,8 @@ hipError_t launch_quant_gemv(const uint8_t* w, int64_t N, int64_t K, const float
   const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows));
   Params p{w, (int)N, (int)K, q, d, y, g.lshift, g.wk, g.J, nullptr, 0, nullptr, 1, 0,
            a, q, d};
-  hipLaunchKernelGGL((gemv_kernel<1, 1, false, true>), grid, dim3(64 * g.wk), lds_bytes(1, g),
-                     stream, p);
+  const GemvFn fn = qh == 1 ? gemv_kernel<1, 1, false, 1> : gemv_kernel<1, 1, false, 2>;
+  hipLaunchKernelGGL(fn, grid, dim3(64 * g.wk), lds_bytes(1, g), stream, p);
   return hipGetLastError();
 }
 
@@ -308,7 +327,8 @@ hipError_t launch_quant_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t
                                  int8_t* q, float* d, float* y, int32_t* err,
                                  hipStream_t stream) {
   Geometry g;
-  if (!quant_geometry(K, N * top_k, top_k * N * (K / 32) * 10, g)) {
+  const int qh = quant_geometry(K, N * top_k, top_k * N * (K / 32) * 10, g);
+  if (qh == 0) {
     const hipError_t e = launch_quantize_acts(a, 1, K, q, d, stream);
     if (e != hipSuccess) return e;
     return launch_moe_gemv(w, E, N, K, ids, top_k, q, d, y, err, stream);
@@ -316,8 +336,8 @@ hipError_t launch_quant_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t
   const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows), (uint32_t)top_k);
   Params p{w, (int)N, (int)K, q, d, y, g.lshift, g.wk, g.J, ids, (int)E, err, (int)top_k,
            (int)top_k, a, q, d};
-  hipLaunchKernelGGL((gemv_kernel<1, 1, true, true>), grid, dim3(64 * g.wk), lds_bytes(1, g),
-                     stream, p);
+  const GemvFn fn = qh == 1 ? gemv_kernel<1, 1, true, 1> : gemv_kernel<1, 1, true, 2>;
+  hipLaunchKernelGGL(fn, grid, dim3(64 * g.wk), lds_bytes(1, g), stream, p);
   return hipGetLastError();
 }
 

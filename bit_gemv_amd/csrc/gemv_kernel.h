@@ -35,15 +35,6 @@ struct Params {
   float* dout;
 };
 
-// Decode one 80-byte group held in registers and accumulate its product with
-// M activation columns.  `act` points at the LDS activations of column 0 for
-// this group and `dact` at its 8 block scales; columns are `act_stride` and
-// `d_stride` dwords apart.  Up to four columns, a block's activations are
-// read from LDS one block ahead of its products, so that their latency hides
-// behind the previous block's vector work (measured at 16384 x 5120: M = 1,
-// 2, 4 take 2, 5 and 7 % less time); with more columns the extra registers
-// cost more waves per SIMD than the latency they hide (M = 8: 15 % slower),
-// and each block reads its own activations.
 // Block jb of the group against the M columns; acts(m, A0, A1, d) supplies
 // column m's activations (two words of 16 int8) and block scale.
 template <int M, typename Acts>
@@ -237,6 +228,34 @@ __device__ __forceinline__ void load_acts_and_chunk(const float* abase, uint32_t
       : "memory");
 }
 
+// The same for two halves per lane: 2 x 16 fp32 activations at abase + aoff0
+// and abase + aoff1, then the weight chunk, then a wait for the activations.
+__device__ __forceinline__ void load_acts2_and_chunk(const float* abase, uint32_t aoff0,
+                                                     uint32_t aoff1, const uint8_t* wbase,
+                                                     const ChunkOffsets& o, uint32_t m0v,
+                                                     v4f (&x)[4], v4f (&z)[4]) {
+  asm volatile(
+      "global_load_dwordx4 %0, %8, %10\n\t"
+      "global_load_dwordx4 %1, %8, %10 offset:16\n\t"
+      "global_load_dwordx4 %2, %8, %10 offset:32\n\t"
+      "global_load_dwordx4 %3, %8, %10 offset:48\n\t"
+      "global_load_dwordx4 %4, %9, %10\n\t"
+      "global_load_dwordx4 %5, %9, %10 offset:16\n\t"
+      "global_load_dwordx4 %6, %9, %10 offset:32\n\t"
+      "global_load_dwordx4 %7, %9, %10 offset:48\n\t"
+      "s_mov_b32 m0, %16\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %11, %17\n\t"
+      "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %12, %17\n\t"
+      "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %13, %17\n\t"
+      "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %14, %17\n\t"
+      "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %15, %17\n\t"
+      "s_waitcnt vmcnt(5)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(z[0]), "=&v"(z[1]),
+        "=&v"(z[2]), "=&v"(z[3])
+      : "v"(aoff0), "v"(aoff1), "s"(abase), "v"(o.off[0]), "v"(o.off[1]), "v"(o.off[2]),
+        "v"(o.off[3]), "v"(o.off[4]), "s"(m0v), "s"(wbase)
+      : "memory");
+}
+
 // Quantize the 16 fp32 activations of one half in place of the separate
 // activation kernel, with its exact arithmetic: the block's max |a| comes
 // from this lane and its partner (the other half of the block, lane ^ 1),
@@ -354,9 +373,12 @@ __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)"
 // as soon as it has landed.  Each wave stages the activations of its own
 // groups, so no workgroup barrier precedes the products; one barrier
 // precedes the final cross-wave sum.  M activation columns; MOE selects the
-// weight matrix through ids[blockIdx.y].
-template <int M, int JT, bool MOE, bool QA>
+// weight matrix through ids[blockIdx.y].  QH > 0: the quantizing form, each
+// lane quantizing QH (1 or 2) halves of the wave's activation slice.
+template <int M, int JT, bool MOE, int QH>
 __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
+  constexpr bool QA = QH > 0;
+  static_assert(QH >= 0 && QH <= 2, "one or two halves per lane");
   static_assert(!QA || (M == 1 && JT == 1), "the quantizing form is one column, one chunk");
   extern __shared__ uint32_t lds[];
   const int K = p.K, N = p.N;
@@ -450,29 +472,44 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
 
   const uint32_t ring_m0 = lds_m0(wlds);
   if constexpr (QA) {
-    // Quantizing form: lane h of the wave takes half h of the wave's slice
-    // (ag*16 <= 64 halves; lanes past the end repeat the last one and write
-    // nothing), loads its fp32 activations and the weight chunk in one go,
-    // quantizes while the weights stream, and writes the int8 half (in the
-    // lane order of the expanded weights) and the block scale to the same
-    // LDS slots the loaded form uses.  Workgroup 0 also writes q and d out.
+    // Quantizing form: lane l of the wave takes halves l, l + 64, ... (QH of
+    // them) of the wave's slice (ag*16 <= 64 * QH halves; lanes past the end
+    // repeat the last half and write nothing), loads their fp32 activations
+    // and the weight chunk in one go, quantizes while the weights stream, and
+    // writes each int8 half (in the lane order of the expanded weights) and
+    // its block scale to the same LDS slots the loaded form uses.  Workgroup
+    // 0 also writes q and d out.  A block's two halves sit in lanes 2k and
+    // 2k + 1 of the same round, which share the block maximum.
     const int n_halves = ag * 16;
-    const int h = min(lane, n_halves - 1);
-    const int lgl = h >> 4, piece = h & 15;
-    const int grp = group_of(lgl);
-    v4f x[4];
-    load_acts_and_chunk(p.a, (uint32_t)((grp * 256 + piece * 16) * 4),
-                        wb + (int64_t)(wave << ls) * 80, co, ring_m0, x);
-    uint32_t A[4];
-    const float dv = quantize_half(x, A);
-    if (lane < n_halves) {
-      reinterpret_cast<uint4*>(alds)[lgl * kGroupPieces + piece] = make_uint4(A[0], A[1], A[2], A[3]);
-      if ((piece & 1) == 0) dlds[lgl * 8 + (piece >> 1)] = dv;
-      if (blockIdx.x == 0 && (!MOE || blockIdx.y == 0)) {
-        uint32_t X[4];                 // the transpose is its own inverse
-        transpose_half(A, X);
-        reinterpret_cast<uint4*>(p.qo)[grp * 16 + piece] = make_uint4(X[0], X[1], X[2], X[3]);
-        if ((piece & 1) == 0) p.dout[grp * 8 + (piece >> 1)] = dv;
+    int hs[QH], aoffs[QH];
+#pragma unroll
+    for (int r = 0; r < QH; ++r) {
+      hs[r] = min(lane + 64 * r, n_halves - 1);
+      aoffs[r] = (group_of(hs[r] >> 4) * 256 + (hs[r] & 15) * 16) * 4;
+    }
+    v4f x[QH][4];
+    if constexpr (QH == 1)
+      load_acts_and_chunk(p.a, (uint32_t)aoffs[0], wb + (int64_t)(wave << ls) * 80, co,
+                          ring_m0, x[0]);
+    else
+      load_acts2_and_chunk(p.a, (uint32_t)aoffs[0], (uint32_t)aoffs[QH - 1],
+                           wb + (int64_t)(wave << ls) * 80, co, ring_m0, x[0], x[QH - 1]);
+#pragma unroll
+    for (int r = 0; r < QH; ++r) {
+      uint32_t A[4];
+      const float dv = quantize_half(x[r], A);
+      const int lgl = hs[r] >> 4, piece = hs[r] & 15;
+      if (lane + 64 * r < n_halves) {
+        reinterpret_cast<uint4*>(alds)[lgl * kGroupPieces + piece] =
+            make_uint4(A[0], A[1], A[2], A[3]);
+        if ((piece & 1) == 0) dlds[lgl * 8 + (piece >> 1)] = dv;
+        if (blockIdx.x == 0 && (!MOE || blockIdx.y == 0)) {
+          const int grp = group_of(lgl);
+          uint32_t X[4];                 // the transpose is its own inverse
+          transpose_half(A, X);
+          reinterpret_cast<uint4*>(p.qo)[grp * 16 + piece] = make_uint4(X[0], X[1], X[2], X[3]);
+          if ((piece & 1) == 0) p.dout[grp * 8 + (piece >> 1)] = dv;
+        }
       }
     }
   } else {
@@ -599,10 +636,10 @@ constexpr int kMaxChunksInFlight = 4;
 template <int M, bool MOE>
 GemvFn pick(int jt) {
   switch (jt) {
-    case 1: return gemv_kernel<M, 1, MOE, false>;
-    case 2: return gemv_kernel<M, 2, MOE, false>;
-    case 3: return gemv_kernel<M, 3, MOE, false>;
-    default: return gemv_kernel<M, 4, MOE, false>;
+    case 1: return gemv_kernel<M, 1, MOE, 0>;
+    case 2: return gemv_kernel<M, 2, MOE, 0>;
+    case 3: return gemv_kernel<M, 3, MOE, 0>;
+    default: return gemv_kernel<M, 4, MOE, 0>;
   }
 }
 

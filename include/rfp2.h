@@ -250,8 +250,9 @@ rfp2_status rfp2_moe_gemm(const uint8_t* w, int64_t E, int64_t N, int64_t K,
  * are faster): each wave quantizes the activations it needs while its
  * weights stream in.  q and d are bit-identical to rfp2_quantize_acts, and y
  * to rfp2_gemv with M = 1 on them, except for K = 6144 and 8192 up to 64 MiB
- * of weights: there the single launch spreads K over more waves than
- * rfp2_gemv does, so y sums in another order (same fp32 bound).
+ * of weights and K = 12288 and 16384 up to 48 MiB: there the single launch
+ * spreads K over more waves than rfp2_gemv does, so y sums in another order
+ * (same fp32 bound).
  *   w [N][K/32][10] bytes, 16-byte aligned.   a [K] fp32, 16-byte aligned.
  *   q [K] int8, 16-byte aligned (written).     d [K/32] fp32, 4-byte aligned
  *   (written).                                 y [N] fp32, 4-byte aligned.

@@ -51,10 +51,12 @@ def boundary_activations(K: int, seed: int) -> np.ndarray:
     return a
 
 
-# K whose one-column split puts 8 groups on each wave: up to 64 MiB of weights
-# the quantizing launch takes a split with at most 4 groups per wave (more
-# waves), so its y sums in another order than rfp2_gemv's
-OWN_SPLIT_K = (6144, 8192)
+# K whose one-column split puts 8 groups (6144, 8192) or 16 groups (12288,
+# 16384) on each wave: at the sizes here the quantizing launch takes a split
+# with at most 4 or 8 groups per wave (more waves), so its y sums in another
+# order than rfp2_gemv's.  At K = 10240 and 14336 it keeps the one-column
+# split (8 groups, two halves per lane) and y is bit-identical.
+OWN_SPLIT_K = (6144, 8192, 12288, 16384)
 
 
 def same_y(y1, y2, K, ref, absref, what):
@@ -79,10 +81,12 @@ def run_both(packed, N, K, a):
     return (host(y1), host(q1), host(d1)), (host(y2), host(q2), host(d2))
 
 
-# K/256 = 1, 3, 5, 8, 16, 20, 28 groups (fused), 56, 64 and 128 (the wave's
-# slice exceeds 64 halves: quantization kernel + product); ragged row counts
+# K/256 = 1, 3, 5, 8, 16, 20, 24, 28, 32 groups (one half per lane), 40, 48,
+# 56, 64 (two halves per lane) and 128 (quantization kernel + product);
+# ragged row counts
 SHAPES = [(300, 256), (257, 768), (123, 1280), (513, 2048), (96, 4096), (1000, 5120),
-          (300, 6144), (130, 7168), (129, 8192), (50, 14336), (64, 16384), (37, 32768)]
+          (300, 6144), (130, 7168), (129, 8192), (77, 10240), (90, 12288), (50, 14336),
+          (64, 16384), (37, 32768)]
 
 
 @pytest.mark.parametrize("N,K", SHAPES)
@@ -101,7 +105,7 @@ def test_quant_gemv_matches_two_calls(N, K):
     assert_within_bound(y1, ref, absref, f"quant_gemv {N}x{K}")
 
 
-@pytest.mark.parametrize("K", [2048, 5120, 8192])
+@pytest.mark.parametrize("K", [2048, 5120, 8192, 14336])
 def test_quant_gemv_rounding_boundaries_and_special_blocks(K):
     announce("quant_gemv boundaries", K)
     N = 200
@@ -146,7 +150,7 @@ def test_quant_gemv_full_size_matches_two_calls():
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
 
 
-@pytest.mark.parametrize("K", [4096, 8192])
+@pytest.mark.parametrize("K", [4096, 8192, 14336])
 def test_quant_moe_gemv_matches_two_calls(K):
     announce("quant_moe_gemv", K)
     E, N = 6, 300
