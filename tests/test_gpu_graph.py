@@ -27,6 +27,7 @@ def test_graph_replays_match_eager():
     y1 = empty((M, N), torch.float32)
     y2 = empty((M, N), torch.float32)
     y3 = empty((3, N), torch.float32)
+    torch.cuda.synchronize()          # the inputs were written on the default stream
     s = torch.cuda.Stream(device=dev)
 
     def run():

@@ -182,6 +182,7 @@ def test_moe_gemm_graph_replays_match_eager():
     q, d = to_dev(q), to_dev(d)
     ws = empty(rf.rfp2_moe_gemm_workspace_bytes(E, T, top_k), torch.uint8)
     y = empty((T * top_k, N), torch.float32)
+    torch.cuda.synchronize()          # the inputs were written on the default stream
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         rf.rfp2_moe_gemm(bank, E, N, K, ids, T, top_k, q, d, y, None, ws, s)

@@ -183,13 +183,15 @@ def test_quant_moe_gemv_matches_two_calls(K):
     assert_within_bound(y1[ok], ref[ok], absref, f"quant_moe_gemv K={K}")
 
 
-def test_quant_gemv_graph_replays_match_eager():
-    announce("quant_gemv graph")
-    N, K = 4096, 4096
+# one and two halves per lane
+@pytest.mark.parametrize("N,K", [(4096, 4096), (1024, 14336)])
+def test_quant_gemv_graph_replays_match_eager(N, K):
+    announce("quant_gemv graph", N, K)
     packed = random_blocks(N, K, seed=123, scale_hi=0x28)
     w = to_dev(packed.reshape(-1))
     a = to_dev(synth.activations(1, K, seed=9)[0])
     q, d, y = empty(K, torch.int8), empty(K // 32, torch.float32), empty(N, torch.float32)
+    torch.cuda.synchronize()          # the inputs were written on the default stream
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         rf.rfp2_quant_gemv(w, N, K, a, q, d, y, s)
