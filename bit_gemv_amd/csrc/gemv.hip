@@ -271,17 +271,19 @@ hipError_t launch_moe_gemv_tokens(const uint8_t* w, int64_t E, int64_t N, int64_
 // with at most 4 groups per wave instead (6 or 8 waves) up to 64 MiB: at
 // K = 8192 and 5, 10, 20, 40, 60 MiB of weights 4.8 / 5.2 / 7.5 / 12.0 /
 // 17.6 us against 6.4 / 7.5 / 9.0 / 13.6 / 17.6 us as two launches, within
-// 2 % either way from 50 to 80 MiB.  Wider still, each lane quantizes two
-// halves (8 groups per wave): with the one-column geometry where it gives 8
-// groups (K = 10240 on 5 waves, 14336 on 7) up to 24 MiB (K = 14336 at 8.8 /
-// 17.5 / 35 / 61 MiB: 6.1 / 7.9 / 14.3 / 20.6 us against 7.6 / 9.1 / 14.0 /
-// 20.3 us), and with the best geometry of at most 8 groups where the
-// one-column one gives 16 (K = 12288 on 6 waves, 16384 on 8) up to 48 MiB
-// (K = 16384 at 20 / 40 MiB: 8.1 / 14.0 us against 10.7 / 15.6 us).
+// 2 % either way from 50 to 80 MiB.  Wider still (K = 10240 ... 16384), each
+// lane quantizes two halves (8 groups per wave) up to 64 MiB: with two groups
+// per lane and 4 lanes per row (16 rows per workgroup, so each workgroup's
+// quantization serves twice the rows of a one-group split) when that still
+// gives every compute unit a workgroup, else with one group per lane (8
+// rows).  Against two launches: K = 14336 at 17.5 / 35 / 61 MiB 7.4 / 11.2
+// / 19.3 us against 9.1 / 14.0 / 20.3 us; K = 16384 at 20 / 40 / 60 MiB 7.6 /
+// 12.0 / 16.5 us against 10.7 / 15.6 / 21.1 us; with 2048 rows (128
+// workgroups of 16 rows) the 8-row split is 11-13 % faster than the 16-row
+// one.
 constexpr int64_t kMaxFusedWeightBytes = int64_t(128) << 20;
 constexpr int64_t kMaxFusedOwnGeometryBytes = int64_t(64) << 20;
-constexpr int64_t kMaxFusedTwoHalvesBytes = int64_t(24) << 20;
-constexpr int64_t kMaxFusedTwoHalvesOwnGeometryBytes = int64_t(48) << 20;
+constexpr int64_t kMaxFusedTwoHalvesBytes = int64_t(64) << 20;
 constexpr int kMaxFusedGroups = 4;        // one half per lane
 constexpr int kMaxFusedGroups2 = 8;       // two halves per lane
 
@@ -298,9 +300,15 @@ int quant_geometry(int64_t K, int64_t rows_total, int64_t weight_bytes, Geometry
     g = f;
     return 1;
   }
-  if (ag <= kMaxFusedGroups2) return weight_bytes <= kMaxFusedTwoHalvesBytes ? 2 : 0;
+  if (weight_bytes > kMaxFusedTwoHalvesBytes) return 0;
+  f = pick_geometry(K, 2, kMaxFusedGroups2);
+  if (f.wk > 0 && (rows_total + f.rows - 1) / f.rows >= compute_units()) {
+    g = f;
+    return 2;
+  }
+  if (ag <= kMaxFusedGroups2) return 2;
   f = pick_geometry(K, 1, kMaxFusedGroups2);
-  if (f.wk == 0 || weight_bytes > kMaxFusedTwoHalvesOwnGeometryBytes) return 0;
+  if (f.wk == 0) return 0;                // no split gives every wave <= 8 groups
   g = f;
   return 2;
 }

@@ -248,11 +248,13 @@ rfp2_status rfp2_moe_gemm(const uint8_t* w, int64_t E, int64_t N, int64_t K,
  * activation operand, its scale, then the product), in a single kernel
  * launch for most K and up to 128 MiB of weights (beyond, the two launches
  * are faster): each wave quantizes the activations it needs while its
- * weights stream in.  q and d are bit-identical to rfp2_quantize_acts, and y
- * to rfp2_gemv with M = 1 on them, except for K = 6144 and 8192 up to 64 MiB
- * of weights and K = 12288 and 16384 up to 48 MiB: there the single launch
- * spreads K over more waves than rfp2_gemv does, so y sums in another order
- * (same fp32 bound).
+ * weights stream in.  q and d are bit-identical to rfp2_quantize_acts.  y is
+ * bit-identical to rfp2_gemv with M = 1 on them wherever the single launch
+ * splits K as rfp2_gemv does; where rfp2_gemv's split gives a wave more than
+ * 4 groups of 256 (K = 6144, 8192, 10240, 12288, 14336, 16384) and the call
+ * reads at most 64 MiB, the single launch may split K over more waves or
+ * more rows per workgroup, and y then sums in another order (same fp32
+ * bound).
  *   w [N][K/32][10] bytes, 16-byte aligned.   a [K] fp32, 16-byte aligned.
  *   q [K] int8, 16-byte aligned (written).     d [K/32] fp32, 4-byte aligned
  *   (written).                                 y [N] fp32, 4-byte aligned.

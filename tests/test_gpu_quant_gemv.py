@@ -54,8 +54,9 @@ def boundary_activations(K: int, seed: int) -> np.ndarray:
 # K whose one-column split puts 8 groups (6144, 8192) or 16 groups (12288,
 # 16384) on each wave: at the sizes here the quantizing launch takes a split
 # with at most 4 or 8 groups per wave (more waves), so its y sums in another
-# order than rfp2_gemv's.  At K = 10240 and 14336 it keeps the one-column
-# split (8 groups, two halves per lane) and y is bit-identical.
+# order than rfp2_gemv's.  At K = 10240 and 14336 with fewer rows than 16 per
+# compute unit it keeps the one-column split (8 groups, two halves per lane)
+# and y is bit-identical; with more rows it takes a 16-row split (below).
 OWN_SPLIT_K = (6144, 8192, 12288, 16384)
 
 
@@ -103,6 +104,27 @@ def test_quant_gemv_matches_two_calls(N, K):
     absref = oracle.abs_product_sums(packed, N, K, q_ref, d_ref)[0]
     same_y(y1, y2, K, ref, absref, f"quant_gemv {N}x{K}")
     assert_within_bound(y1, ref, absref, f"quant_gemv {N}x{K}")
+
+
+@pytest.mark.parametrize("N,K", [(4100, 10240), (4096, 14336)])
+def test_quant_gemv_sixteen_row_split(N, K):
+    # enough rows for a 16-row workgroup on every compute unit: two halves per
+    # lane, two groups per lane; q and d bit for bit, y within the fp32 bound
+    # of the oracle on sampled rows (and so is the two-call y)
+    announce("quant_gemv 16-row split", N, K)
+    packed = random_blocks(N, K, seed=N + K, scale_lo=0x00, scale_hi=0x30)
+    a = synth.activations(1, K, seed=K + 1)[0]
+    (y1, q1, d1), (y2, q2, d2) = run_both(packed, N, K, a)
+    q_ref, d_ref = oracle.quantize_acts(a[None, :])
+    assert np.array_equal(q1, q_ref[0]) and np.array_equal(q1, q2)
+    assert np.array_equal(d1.view(np.uint32), d_ref[0].view(np.uint32))
+    assert np.array_equal(d1.view(np.uint32), d2.view(np.uint32))
+    rows = np.unique(np.concatenate([np.arange(0, 16), np.arange(N - 20, N),
+                                     np.random.default_rng(K).choice(N, 48, replace=False)]))
+    ref = oracle.ref_gemv(packed[rows], len(rows), K, q_ref, d_ref)[0]
+    absref = oracle.abs_product_sums(packed[rows], len(rows), K, q_ref, d_ref)[0]
+    assert_within_bound(y1[rows], ref, absref, f"quant_gemv {N}x{K}")
+    assert_within_bound(y2[rows], ref, absref, f"two calls {N}x{K}")
 
 
 @pytest.mark.parametrize("K", [2048, 5120, 8192, 14336])
