@@ -9,8 +9,12 @@
 //     fp32;
 //   * so the per-half weight scales go into the operands, and one fp16 MFMA
 //     pair (K = 16 each) gives the whole 32-weight block's sum
-//     C = s0 * S0 + s1 * S1 directly in fp32 -- exactly, unless the two
-//     halves' scales are more than 2^10 apart, where it rounds once;
+//     C = s0 * S0 + s1 * S1 directly in fp32.  It is exact while the two
+//     halves' scale exponents (E, with E = 0 counted as 1) differ by at most
+//     7: every partial sum is an integer multiple of the smaller scale's
+//     unit below 15 * 8128 * (1 + 2^7) < 2^24.  With a wider split the
+//     core's fp32 accumulation may round, each step within 2^-24 of the
+//     running sum;
 //   * the epilogue per (token, row, block) is one FMA, y += d * C, against
 //     two int->fp32 converts and three FMAs for the int32 per-half partials.
 // The rescale, not the matrix cores, bounds the int8 path; here the two are

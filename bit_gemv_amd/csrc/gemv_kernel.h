@@ -263,12 +263,16 @@ __device__ __forceinline__ void load_acts2_and_chunk(const float* abase, uint32_
 // from zero), d = NaN and q = 0 for a block with a non-finite value, q = 0
 // when d = 0.  |a / d| <= 127 * (1 + 2^-23), so q never needs the clamp to
 // +-127.
-//   * fl32(a / d) is replaced by t = a * rcp(d) (rcp within one ulp), off by
-//     less than 2.7e-5 for |a / d| <= 127.5 whether or not the product is
-//     rounded before the next step (the compiler fuses it into the add);
-//     adding 1.5 * 2^23 rounds t to the nearest integer k and leaves k's
-//     two's-complement low byte in the low byte of the sum.  When
-//     |t - k| < 0.49997, k is roundf(fl32(a / d)) (fl32 adds at most 3.9e-6).
+//   * fl32(a / d) is replaced by t = a * rcp(d); adding 1.5 * 2^23 rounds t
+//     to the nearest integer k and leaves k's two's-complement low byte in
+//     the low byte of the sum.  Error budget, with |a / d| <= 127 * (1 +
+//     2^-23) < 127.00002: rcp is within one ulp (relative error <= 2^-23), so
+//     the exact product a * rcp(d) is within 127.00002 * 2^-23 < 1.52e-5 of
+//     a / d; rounding the product (the compiler may instead fuse it into the
+//     add) moves it by at most half an ulp at 127, 3.9e-6; and fl32(a / d)
+//     is within 3.9e-6 of a / d.  So |t - fl32(a / d)| < 2.3e-5 and, when
+//     |t - k| < 0.49997 = 0.5 - 3e-5, fl32(a / d) lies strictly within 0.5 of
+//     k: k is roundf(fl32(a / d)).
 //   * Otherwise (t within 3e-5 of a half-integer), or when d is subnormal,
 //     the lane redoes its values with the IEEE division and roundf.
 // A receives q packed four per dword in the lane order of the expanded

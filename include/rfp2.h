@@ -141,8 +141,9 @@ rfp2_status rfp2_gemm(const uint8_t* w, int64_t N, int64_t K,
  * matrix cores.  Every reconstructed weight (level x UE4M3 scale) and every
  * int8 activation is exactly an fp16 number and every product is exact in
  * fp32, so each 32-weight block's sum s0*S0 + s1*S1 comes out of the matrix
- * core in fp32 (exact unless its two scales are more than 2^10 apart, where
- * it rounds once) and only the activation scale is applied afterwards: one
+ * core in fp32 (exact while the two scale exponents differ by at most 7;
+ * beyond, the core's fp32 accumulation may round, each step within 2^-24 of
+ * the running sum) and only the activation scale is applied afterwards: one
  * multiply-add per output and block instead of the int32 path's five.
  * Layouts, alignment and limits as rfp2_gemm.
  */

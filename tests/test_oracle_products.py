@@ -21,11 +21,13 @@ _SCALES = [Fraction(v) / 2 for v in
 _LEVELS = (-4, -1, 1, 4)
 
 
-def _exact(packed, N, K, q, d):
-    """Exact y[m][n] and exact per-half integer sums, from the raw bytes."""
+def _exact(packed, N, K, q, d, with_abs=False):
+    """Exact y[m][n], exact per-half integer sums and (with_abs) the exact
+    sum_k |w[n,k] * a[m,k]|, from the raw bytes."""
     M = q.shape[0]
     B = K // 32
     y = [[Fraction(0)] * N for _ in range(M)]
+    ab = [[Fraction(0)] * N for _ in range(M)]
     sums = np.zeros((M, N, B, 2), dtype=np.int64)
     for n in range(N):
         for b in range(B):
@@ -36,9 +38,11 @@ def _exact(packed, N, K, q, d):
                 s = _SCALES[int(blk[8 + i // 16])]
                 for m in range(M):
                     qa = int(q[m, 32 * b + i])
-                    y[m][n] += level * s * qa * Fraction(float(d[m, b]))
+                    term = level * s * qa * Fraction(float(d[m, b]))
+                    y[m][n] += term
+                    ab[m][n] += abs(term)
                     sums[m, n, b, i // 16] += level * qa
-    return y, sums
+    return (y, sums, ab) if with_abs else (y, sums)
 
 
 def _tiny_matrix(N, K, seed, all_bytes=False):
@@ -129,3 +133,51 @@ def test_moe_rows_follow_ids_and_bad_ids_are_nan():
         else:
             assert np.all(np.isnan(y[j]))
     assert np.array_equal(y[0], y[2])            # duplicates are independent copies
+
+
+@pytest.mark.parametrize("N,K,M", CASES)
+def test_abs_product_sums_match_exact_rationals(N, K, M):
+    # The tolerance scale of every GPU comparison, sum_k |w[n,k] * a[m,k]|
+    # ("03 · Runtime": the magnitudes of the terms d_a * s * level * q that
+    # the integer pipeline sums), pinned to an exact evaluation from the raw
+    # bytes.  Every term is exact in fp64 (a level times a UE4M3 scale has at
+    # most 4 significant bits, q * d at most 31), so the oracle's only error
+    # is the fp64 summation of K non-negative terms: at most (K - 1) * 2^-53
+    # relative.  A scaled, shifted, signed or term-dropping variant fails.
+    packed = _tiny_matrix(N, K, seed=N * 1000 + K + 1, all_bytes=(K == 1024))
+    rng = np.random.default_rng(K + M + 1)
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    q, d = oracle.quantize_acts(a)
+    _, _, ab_exact = _exact(packed, N, K, q, d, with_abs=True)
+    absum = oracle.abs_product_sums(packed, N, K, q, d)
+    assert absum.shape == (M, N)
+    rel = Fraction(K, 2 ** 53)
+    for m in range(M):
+        for n in range(N):
+            exact = ab_exact[m][n]
+            assert exact > 0
+            assert abs(Fraction(float(absum[m, n])) - exact) <= rel * exact
+
+
+def test_abs_product_sums_edge_scales_and_signs():
+    # one block per row, chosen by hand: the sum of magnitudes ignores the
+    # signs of levels and activations, takes each half's own scale (0x7E =
+    # 224, 0x01 = 2^-10, 0x00 = 0) and equals |y| when every term has one sign
+    codes = np.zeros((3, 32), np.uint8)
+    codes[0, :16] = 0            # -4 on half 0
+    codes[0, 16:] = 3            # +4 on half 1
+    codes[1] = np.arange(32) % 4
+    codes[2] = 2                 # +1 everywhere
+    eb = np.array([[0x7E, 0x01], [0x38, 0x00], [0x01, 0x7E]], np.uint8)
+    packed = oracle.pack_matrix(codes, eb)
+    q = np.concatenate([np.full(16, -3), np.full(16, 5)]).astype(np.int8)[None, :]
+    d = np.array([[0.25]], np.float32)
+    absum = oracle.abs_product_sums(packed, 3, 32, q, d)
+    lv = np.array([-4, -1, 1, 4])
+    exp0 = 16 * 4 * 224 * 3 * 0.25 + 16 * 4 * 2 ** -10 * 5 * 0.25
+    exp1 = sum(abs(lv[i % 4]) * 0.5 * abs(int(q[0, i])) * 0.25 for i in range(16))
+    exp2 = 16 * 2 ** -10 * 3 * 0.25 + 16 * 224 * 5 * 0.25
+    assert absum[0].tolist() == [exp0, exp1, exp2]
+    y = oracle.ref_gemv(packed, 3, 32, q, d)
+    assert y[0, 0] == absum[0, 0]                 # (-4)(-3) and (+4)(+5): all positive
+    assert abs(y[0, 2]) < absum[0, 2]             # mixed signs cancel in y only
