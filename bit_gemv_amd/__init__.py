@@ -48,6 +48,7 @@ _SIGNATURES = {
                              _c_p, _c_p, _c_p], ctypes.c_int),
     "rfp2_debug_decode": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p], ctypes.c_int),
     "rfp2_debug_half_dots": ([_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
+    "rfp2_debug_decode_f16": ([_c_p, _c_i64, _c_i64, ctypes.c_int, _c_p, _c_p], ctypes.c_int),
 }
 
 
@@ -272,3 +273,11 @@ def rfp2_debug_half_dots(w, N: int, K: int, q, M: int, sums_out, stream=None) ->
         _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), N, K,
         _ptr(q, torch.int8, M * K, "q"), M,
         _ptr(sums_out, torch.int32, M * N * _blocks(K) * 2, "sums_out"), _stream(stream)))
+
+
+def rfp2_debug_decode_f16(w, N: int, K: int, form: int, h_out, stream=None) -> None:
+    """h_out: int16 tensor [N, K] receiving IEEE half-precision bit patterns."""
+    import torch
+    _check("rfp2_debug_decode_f16", lib().rfp2_debug_decode_f16(
+        _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), N, K, int(form),
+        _ptr(h_out, torch.int16, N * K, "h_out"), _stream(stream)))

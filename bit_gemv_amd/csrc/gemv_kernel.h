@@ -35,12 +35,16 @@ struct Params {
   float* dout;
 };
 
-// Block jb of the group against the M columns; acts(m, A0, A1, d) supplies
-// column m's activations (two words of 16 int8) and block scale.
-template <int M, typename Acts>
-__device__ __forceinline__ void block_product(const uint32_t (&dw)[20], int jb, Acts acts,
-                                              float (&acc)[M], uint32_t& bad_lo,
-                                              uint32_t& bad_hi, int ncols) {
+// Decode block jb (0..7) of an 80-byte group held in registers: the eight
+// int8x4 words of its two halves (expand_block's lane order), both scales
+// from one packed fp8 convert (each the UE4M3 value times scale_fix()'s
+// inverse), and the dword holding its scale pair (bytes 0,1 for an even
+// block, 2,3 for an odd one), whose top bits flag bytes 0x80..0xFF.  gfx950
+// converts OCP E4M3FN, where byte 0x7F is NaN, so that byte poisons the
+// products by itself.
+__device__ __forceinline__ void decode_block(const uint32_t (&dw)[20], int jb,
+                                             uint32_t (&W0)[4], uint32_t (&W1)[4],
+                                             float& s0, float& s1, uint32_t& sc) {
   // block jb occupies bytes 10*jb .. 10*jb+9 of the group
   const int o = (10 * jb) / 4;
   uint32_t c0, c1;
@@ -51,15 +55,35 @@ __device__ __forceinline__ void block_product(const uint32_t (&dw)[20], int jb, 
     c0 = __builtin_amdgcn_alignbit(dw[o + 1], dw[o], 16);
     c1 = __builtin_amdgcn_alignbit(dw[o + 2], dw[o + 1], 16);
   }
-  const uint32_t sc = dw[o + 2];   // scale pair: bytes 0,1 (even) or 2,3 (odd)
-  uint32_t W0[4], W1[4];
+  sc = dw[o + 2];
   expand_block(c0, c1, W0, W1);
-  // both scales of the block in one packed fp8 convert.  gfx950 converts
-  // OCP E4M3FN, where byte 0x7F is NaN: it poisons the row through the
-  // product.  Bytes 0x80..0xFF are caught by their top bits, OR-ed into
-  // bad_* (bits 7/15 for an even block, 23/31 for an odd one).
   const float2 sp = (jb & 1) ? fp8_pair<true>(sc) : fp8_pair<false>(sc);
-  const float s0 = sp.x, s1 = sp.y;
+  s0 = sp.x;
+  s1 = sp.y;
+}
+
+// The int32 sums of a block's two halves against one column's activations
+// (each half's 16 int8 in the lane order of the expanded weights).
+__device__ __forceinline__ void block_half_sums(const uint32_t (&W0)[4], const uint32_t (&W1)[4],
+                                                const uint4& A0, const uint4& A1, int32_t& S0,
+                                                int32_t& S1) {
+  const uint32_t a0[4] = {A0.x, A0.y, A0.z, A0.w};
+  const uint32_t a1[4] = {A1.x, A1.y, A1.z, A1.w};
+  S0 = half_dot(W0, a0);
+  S1 = half_dot(W1, a1);
+}
+
+// Block jb of the group against the M columns; acts(m, A0, A1, d) supplies
+// column m's activations (two words of 16 int8) and block scale.  Bytes
+// 0x80..0xFF of the scale pair are OR-ed into bad_* (bits 7/15 for an even
+// block, 23/31 for an odd one).
+template <int M, typename Acts>
+__device__ __forceinline__ void block_product(const uint32_t (&dw)[20], int jb, Acts acts,
+                                              float (&acc)[M], uint32_t& bad_lo,
+                                              uint32_t& bad_hi, int ncols) {
+  uint32_t W0[4], W1[4], sc;
+  float s0, s1;
+  decode_block(dw, jb, W0, W1, s0, s1, sc);
   if ((jb & 1) == 0)
     bad_lo |= sc;
   else
@@ -70,10 +94,8 @@ __device__ __forceinline__ void block_product(const uint32_t (&dw)[20], int jb, 
     uint4 A0, A1;
     float dm;
     acts(m, A0, A1, dm);
-    const uint32_t a0[4] = {A0.x, A0.y, A0.z, A0.w};
-    const uint32_t a1[4] = {A1.x, A1.y, A1.z, A1.w};
-    const int32_t S0 = half_dot(W0, a0);
-    const int32_t S1 = half_dot(W1, a1);
+    int32_t S0, S1;
+    block_half_sums(W0, W1, A0, A1, S0, S1);
     acc[m] = fmaf(dm, fmaf(s1, (float)S1, s0 * (float)S0), acc[m]);
   }
 }

@@ -239,4 +239,15 @@ rfp2_status rfp2_debug_half_dots(const uint8_t* w, int64_t N, int64_t K,
   return from_hip(rfp2::launch_debug_half_dots(w, N, K, q, M, sums_out, stream));
 }
 
+rfp2_status rfp2_debug_decode_f16(const uint8_t* w, int64_t N, int64_t K, int form,
+                                  uint16_t* h_out, hipStream_t stream) {
+  if (!w || !h_out) return RFP2_E_NULL;
+  if (N < 1 || N > kMaxRows || K < 32 || K % 32 != 0 || K > (int64_t(1) << 30) ||
+      (form != 0 && form != 1))
+    return RFP2_E_SHAPE;
+  if (!aligned(w, 2) || !aligned(h_out, 2)) return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(rfp2::launch_debug_decode_f16(w, N, K, form, h_out, stream));
+}
+
 }  // extern "C"

@@ -294,16 +294,32 @@ rfp2_status rfp2_read_ceiling(const uint8_t* buf, int64_t bytes, uint32_t* out,
                               hipStream_t stream);
 
 /*
- * Inspection entry points (they run the same device decode as the products).
+ * Inspection entry points.  They run the products' own device functions on
+ * the register layouts the products use, so what they return is what the
+ * products compute internally ("03 · Runtime": SPREAD / PERMUTE expand each
+ * code byte into four int8 lanes, DOT4 sums each 16-weight half in int32).
  *
- * rfp2_debug_decode: the int8 lane each weight expands to and the fp32 scale
- * of each half.  codes_out [N][K] int8, scales_out [N][K/16] fp32 (NaN for an
- * illegal byte).  Requires N >= 1, K >= 32, K % 32 == 0; w 2-byte aligned.
+ * rfp2_debug_decode: the GEMV's decode.  The block stream is taken in 80-byte
+ * groups of 8 blocks, as a GEMV lane holds them, and each block is decoded as
+ * the GEMV decodes block j of its group (the odd blocks start at byte 2 of a
+ * dword).  codes_out [N][K] int8: the lane each weight expands to;
+ * scales_out [N][K/16] fp32: the scale of each half (NaN for an illegal
+ * byte).  Requires N >= 1, K >= 32, K % 32 == 0; w 2-byte aligned, codes_out
+ * and scales_out 4-byte aligned.
  *
- * rfp2_debug_half_dots: the int32 sum of each 16-weight half against the int8
- * activations, sums_out [M][N][K/32][2] int32.  Requires N >= 1, M >= 1,
- * K >= 32, K % 32 == 0, M * N * (K/32) <= 2^40; w 2-byte aligned, q 4-byte
- * aligned.
+ * rfp2_debug_half_dots: the GEMV's int32 sum of each 16-weight half against
+ * the int8 activations (staged in the GEMV's lane order), sums_out
+ * [M][N][K/32][2] int32.  Requires N >= 1, M >= 1, K >= 32, K % 32 == 0,
+ * M * N * (K/32) <= 2^40; w 2-byte aligned, q 4-byte aligned.
+ *
+ * rfp2_debug_decode_f16: the fp16 value (level x scale) each weight takes in
+ * the fp16 matrix-core products, h_out [N][K] as IEEE half-precision bit
+ * patterns in natural order (NaN for both halves of a block with an illegal
+ * scale byte).  form 0: the decode of rfp2_gemm_f16 (a thread expands both
+ * halves of one block of a 20-byte pair); form 1: the decode of
+ * rfp2_moe_gemm (a lane expands one half of a block straight into its
+ * matrix-core operand).  Requires N >= 1, K >= 32, K % 32 == 0, form 0 or 1;
+ * w and h_out 2-byte aligned.
  */
 rfp2_status rfp2_debug_decode(const uint8_t* w, int64_t N, int64_t K,
                               int8_t* codes_out, float* scales_out,
@@ -311,6 +327,8 @@ rfp2_status rfp2_debug_decode(const uint8_t* w, int64_t N, int64_t K,
 rfp2_status rfp2_debug_half_dots(const uint8_t* w, int64_t N, int64_t K,
                                  const int8_t* q, int64_t M,
                                  int32_t* sums_out, hipStream_t stream);
+rfp2_status rfp2_debug_decode_f16(const uint8_t* w, int64_t N, int64_t K, int form,
+                                  uint16_t* h_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

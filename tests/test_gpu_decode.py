@@ -74,3 +74,85 @@ def test_half_dots_bitexact(N, K, M):
     got = host(sums)
     assert np.array_equal(got.astype(np.int64), ref)
     assert got[0, 0, 0, 0] == 8128
+
+
+def parity_blocks(pairs=256):
+    """Blocks 2t and 2t + 1 identical (t < pairs), so that every byte value
+    sits in an even block (starting on a dword of an 80-byte group) and in an
+    odd one (starting at byte 2 of a dword): code bytes (8t + j) % 256 cover
+    all 256 values at both parities, the scale pair (t % 256, (t + 128) %
+    256) every legal and illegal scale byte in both positions.  -> uint8
+    [2 * pairs * 10]."""
+    t = np.repeat(np.arange(pairs), 2)
+    codes = (8 * t[:, None] + np.arange(8)[None, :]) % 256
+    scales = np.stack([t % 256, (t + 128) % 256], axis=1)
+    return np.concatenate([codes, scales], axis=1).astype(np.uint8).reshape(-1)
+
+
+def _expected_scales(eb):
+    legal = eb <= oracle.UE4M3_MAX_BYTE
+    ref = np.full(eb.shape, np.nan, np.float32)
+    ref[legal] = oracle.ue4m3_table()[eb[legal]].astype(np.float32)
+    return ref
+
+
+@pytest.mark.parametrize("N,K", [(16, 1024), (4, 4096), (3, 96)])
+def test_gemv_group_decode_all_bytes_both_parities(N, K):
+    # the GEMV's own decode (decode_block on an 80-byte group), bit for bit:
+    # every code byte and every scale byte at even and odd block positions
+    announce("debug_decode parity blocks", N, K)
+    flat = parity_blocks(256)
+    packed = np.resize(flat, N * K // 32 * 10).reshape(N, K // 32 * 10)
+    codes, scales = _decode(packed, N, K)
+    assert np.array_equal(codes, oracle.decoded_int8(packed, N, K))
+    _, eb = oracle.unpack_matrix(packed, N, K)
+    ref = _expected_scales(eb)
+    assert np.array_equal(np.isnan(scales), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(scales[ok], ref[ok])
+    if N * K // 32 >= 512:
+        # each legal and illegal byte was seen in both positions, both parities
+        blk = np.arange(N * K // 32)
+        for pos in (0, 1):
+            for par in (0, 1):
+                seen = eb.reshape(-1, 2)[(blk % 2 == par), pos]
+                assert len(np.unique(seen)) == 256
+
+
+@pytest.mark.parametrize("N,K,M", [(16, 1024, 2), (3, 96, 1)])
+def test_gemv_group_half_dots_all_bytes_both_parities(N, K, M):
+    announce("debug_half_dots parity blocks", N, K, M)
+    flat = parity_blocks(256)
+    packed = np.resize(flat, N * K // 32 * 10).reshape(N, K // 32 * 10)
+    q = synth.uniform_bytes(M * K, 0, 254, seed=17 + M).view(np.int8).reshape(M, K)
+    q = np.where(q == -128, -127, q).astype(np.int8)
+    q[0, :64] = 127                          # extremes on an even and an odd block
+    q[-1, 64:128] = -127
+    sums = empty((M, N, K // 32, 2), torch.int32)
+    rf.rfp2_debug_half_dots(to_dev(packed.reshape(-1)), N, K, to_dev(q), M, sums)
+    got = host(sums).astype(np.int64)
+    assert np.array_equal(got, oracle.half_sums(packed, N, K, q))
+
+
+@pytest.mark.parametrize("form", [0, 1])
+@pytest.mark.parametrize("N,K", [(16, 1024), (3, 96), (5, 32)])
+def test_f16_decode_bitexact(form, N, K):
+    # the fp16 matrix-core kernels' decode (form 0: rfp2_gemm_f16's staging;
+    # form 1: rfp2_moe_gemm's per-lane operand decode), bit for bit against
+    # level * scale in IEEE half precision; a block with an illegal scale byte
+    # is NaN in both halves
+    announce("debug_decode_f16", form, N, K)
+    flat = parity_blocks(256)
+    packed = np.resize(flat, N * K // 32 * 10).reshape(N, K // 32 * 10)
+    h = empty((N, K), torch.int16)
+    rf.rfp2_debug_decode_f16(to_dev(packed.reshape(-1)), N, K, form, h)
+    got = host(h).view(np.float16)
+    codes, eb = oracle.unpack_matrix(packed, N, K)
+    eb_blk = eb.reshape(N, K // 32, 2)
+    bad_blk = (eb_blk > oracle.UE4M3_MAX_BYTE).any(axis=2)             # [N, B]
+    clean = packed.copy().reshape(N, K // 32, 10)
+    clean[..., 8:10] = np.where(clean[..., 8:10] > 0x7E, 0x38, clean[..., 8:10])
+    ref = oracle.dequantize_weights(clean.reshape(N, -1), N, K).astype(np.float16)
+    bad = np.repeat(bad_blk, 32, axis=1)
+    assert np.isnan(got[bad]).all()
+    assert np.array_equal(got[~bad].view(np.uint16), ref[~bad].view(np.uint16))
