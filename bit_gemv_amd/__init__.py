@@ -42,6 +42,8 @@ _SIGNATURES = {
     "rfp2_moe_gemm_workspace_bytes": ([_c_i64, _c_i64, _c_i64], ctypes.c_size_t),
     "rfp2_moe_gemm": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p,
                        _c_p, _c_p, ctypes.c_size_t, _c_p], ctypes.c_int),
+    "rfp2_moe_gemm_noalloc": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_i64, _c_p, _c_p,
+                               _c_p, _c_p, _c_p], ctypes.c_int),
     "rfp2_read_ceiling": ([_c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
     "rfp2_quant_gemv": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p], ctypes.c_int),
     "rfp2_quant_moe_gemv": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p,
@@ -227,6 +229,20 @@ def rfp2_moe_gemm(w, E: int, N: int, K: int, ids, T: int, top_k: int, q, d, y, e
 
 
 READ_CEILING_OUTPUTS = 2048
+
+
+MOE_GEMM_NOALLOC_MAX_BYTES = 1 << 20
+
+
+def rfp2_moe_gemm_noalloc(w, E: int, N: int, K: int, ids, T: int, top_k: int, q, d, y,
+                          err=None, stream=None) -> None:
+    import torch
+    errp = None if err is None else _ptr(err, torch.int32, 1, "err")
+    _check("rfp2_moe_gemm_noalloc", lib().rfp2_moe_gemm_noalloc(
+        _ptr(w, torch.uint8, E * N * _blocks(K) * 10, "w"), E, N, K,
+        _ptr(ids, torch.int32, T * top_k, "ids"), T, top_k,
+        _ptr(q, torch.int8, T * K, "q"), _ptr(d, torch.float32, T * _blocks(K), "d"),
+        _ptr(y, torch.float32, T * top_k * N, "y"), errp, _stream(stream)))
 
 
 def rfp2_read_ceiling(buf, nbytes: int, out, stream=None) -> None:

@@ -177,6 +177,27 @@ rfp2_status rfp2_moe_gemm(const uint8_t* w, int64_t E, int64_t N, int64_t K,
                                         stream));
 }
 
+static_assert(RFP2_MOE_GEMM_NOALLOC_MAX_BYTES == rfp2::kNoallocScratchBytes,
+              "the header's limit is the size of the library's scratch array");
+
+rfp2_status rfp2_moe_gemm_noalloc(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                                  const int32_t* ids, int64_t T, int64_t top_k,
+                                  const int8_t* q, const float* d, float* y, int32_t* err,
+                                  hipStream_t stream) {
+  if (!w || !ids || !q || !d || !y) return RFP2_E_NULL;
+  const size_t need = rfp2_moe_gemm_workspace_bytes(E, T, top_k);
+  if (need == 0 || need > RFP2_MOE_GEMM_NOALLOC_MAX_BYTES || N < 1 || N > kMaxRows ||
+      K < 256 || K % 256 != 0 || K > (int64_t(1) << 24))
+    return RFP2_E_SHAPE;
+  if (rfp2::moe_gemm_max_grid(E, N, T * top_k) > (int64_t(1) << 31) - 1) return RFP2_E_SHAPE;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(d, 4) || !aligned(y, 4) ||
+      !aligned(ids, 4) || (err && !aligned(err, 4)))
+    return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(
+      rfp2::launch_moe_gemm_noalloc(w, E, N, K, ids, T, top_k, q, d, y, err, stream));
+}
+
 rfp2_status rfp2_read_ceiling(const uint8_t* buf, int64_t bytes, uint32_t* out,
                               hipStream_t stream) {
   if (!buf || !out) return RFP2_E_NULL;

@@ -243,6 +243,30 @@ rfp2_status rfp2_moe_gemm(const uint8_t* w, int64_t E, int64_t N, int64_t K,
                           size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * rfp2_moe_gemm_noalloc -- rfp2_moe_gemm for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same sort and product kernels and the same
+ * result, with the sorted slots kept in a device array that the library owns
+ * instead of a caller workspace.  The call allocates nothing.
+ *   w, ids, q, d, y, err and their layouts, alignment and limits as
+ *   rfp2_moe_gemm; in addition rfp2_moe_gemm_workspace_bytes(E, T, top_k)
+ *   must not exceed RFP2_MOE_GEMM_NOALLOC_MAX_BYTES (otherwise RFP2_E_SHAPE,
+ *   nothing launched).  With 128 experts that allows up to 261,886 routed
+ *   slots, e.g. 32,735 tokens at top-8.
+ * The array (RFP2_MOE_GEMM_NOALLOC_MAX_BYTES bytes) is held by every GPU the
+ * library runs on until the process ends; its device address is looked up on
+ * the first call on each device (RFP2_E_LAUNCH if that fails).  All calls on
+ * one GPU share it and it keeps the last call's contents: calls that overlap
+ * in time on one GPU (several streams, several host threads) race and must be
+ * serialised by the caller.
+ */
+#define RFP2_MOE_GEMM_NOALLOC_MAX_BYTES 1048576
+rfp2_status rfp2_moe_gemm_noalloc(const uint8_t* w, int64_t E, int64_t N, int64_t K,
+                                  const int32_t* ids, int64_t T, int64_t top_k,
+                                  const int8_t* q, const float* d, float* y, int32_t* err,
+                                  hipStream_t stream);
+
+/*
  * rfp2_quant_gemv -- one token end to end: quantizes the fp32 activations a
  * exactly as rfp2_quantize_acts does, writing q and d, and computes
  * y = W * a as rfp2_gemv does from that q and d ("03 · Runtime": the int8

@@ -46,6 +46,10 @@ int main(void) {
   expect("moe_gemm_workspace_bytes", rfp2_moe_gemm_workspace_bytes(2, 4, 1) > 0, 1);
   expect("moe_gemm", rfp2_moe_gemm(p, 2, N_, K_, p, 4, 1, p, p, p, NULL, NULL, 0, st),
          RFP2_E_NULL);
+  expect("moe_gemm_noalloc",
+         rfp2_moe_gemm_noalloc(p, 2, N_, K_, p, 4, 1, p, p, NULL, NULL, st), RFP2_E_NULL);
+  expect("moe_gemm_noalloc",
+         rfp2_moe_gemm_noalloc(p, 128, N_, K_, p, 32736, 8, p, p, p, NULL, st), RFP2_E_SHAPE);
   expect("quant_gemv", rfp2_quant_gemv(p, N_, K_, NULL, p, p, p, st), RFP2_E_NULL);
   expect("quant_moe_gemv",
          rfp2_quant_moe_gemv(p, 2, N_, K_, p, 1, p, p, p, NULL, NULL, st), RFP2_E_NULL);

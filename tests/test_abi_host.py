@@ -95,6 +95,17 @@ def test_moe_sort_and_moe_gemm_argument_checks():
     assert gemm(q=MIS) == rf.RFP2_E_ALIGN
     assert gemm(err=P + 1) == rf.RFP2_E_ALIGN
 
+    # the allocation-free form: the same checks, and no batch whose sorted
+    # slots exceed its 1 MiB array (refused before any HIP call)
+    def noalloc(E=8, N=64, K=256, T=512, top_k=8, ids=P, q=P):
+        return L.rfp2_moe_gemm_noalloc(P, E, N, K, ids, T, top_k, q, P, P, None, None)
+    assert noalloc(ids=None) == rf.RFP2_E_NULL
+    assert noalloc(K=320) == rf.RFP2_E_SHAPE
+    assert noalloc(E=2049) == rf.RFP2_E_SHAPE
+    assert noalloc(E=128, T=32736) == rf.RFP2_E_SHAPE        # 261,888 slots: over 1 MiB
+    assert L.rfp2_moe_gemm_workspace_bytes(128, 32735, 8) <= rf.MOE_GEMM_NOALLOC_MAX_BYTES
+    assert noalloc(q=MIS) == rf.RFP2_E_ALIGN
+
 
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
