@@ -9,13 +9,16 @@ quantizing launch (rfp2_quant_gemv / rfp2_quant_moe_gemv; --two-launch
 splits it); otherwise rfp2_quantize_acts followed by the product
 (rfp2_gemv, rfp2_moe_gemv_tokens, rfp2_gemm, rfp2_gemm_f16, or
 rfp2_moe_sort + the grouped routed GEMM, by workload).  The weights are
-quantized on the GPU (rfp2_quantize_weights) before timing, and the step
-rotates over enough distinct copies of them (>= 1 GiB in all) that every
-step reads its weights from HBM rather than from the 256 MB last-level cache.
+quantized on the GPU (rfp2_quantize_weights) before timing, and consecutive
+steps read distinct copies of them: a copy comes back only after >= 1 GiB of
+other weight bytes that the steps actually read (the routed experts only, for
+the MoE workloads), so every step reads its weights from HBM rather than from
+the 256 MB last-level cache.
 
-Timed steps are replayed from HIP graphs of up to 64 consecutive steps (each
-replay checked bit for bit against an eager step), so host launch cost does
-not set the pace.  One JSON line is printed.  `value` is whole-job
+Timed steps are replayed from a ring of HIP graphs, each holding up to 64
+consecutive steps on its own copies (replays checked bit for bit against an
+eager step), so host launch cost does not set the pace; one untimed pass over
+the whole ring precedes the timed replays.  One JSON line is printed.  `value` is whole-job
 throughput (algorithmic bytes of the step / wall time of the step for GEMV
 workloads, 2*M*N*K / step time for the GEMM workload).  `roofline` describes
 the product kernel alone: HIP events on the bench stream around graph
@@ -45,8 +48,10 @@ COLD_BYTES = 1 << 30           # distinct weight bytes rotated through
 # The large-layer GEMV is the workload on which an HBM fraction is meaningful
 # (25 MiB of weights; the 5 MiB projection is latency-bound on this GPU).
 DEFAULT_WORKLOAD = "gemv_16384x5120"
-SECONDARY = ["gemv_4096x4096", "moe_128x1536x4096_top8_t4", "gemm_512x14336x4096",
+SECONDARY = ["gemv_512x2048", "gemv_4096x4096", "moe_128x1536x4096_top8",
+             "gemv_16384x5120_m4", "moe_128x1536x4096_top8_t4", "gemm_512x14336x4096",
              "gemm_f16_512x14336x4096", "moe_gemm_128x1536x4096_top8_t512"]
+MAX_COPY_BYTES = 40 << 30      # device memory the weight copies may take
 KERNEL_SOURCES = ["rfp2_device.h", "gemv_kernel.h", "gemv.hip", "gemv_moe.hip", "gemm.hip",
                   "gemm_f16.hip", "moe_sort.hip", "quantize.hip"]
 
@@ -87,10 +92,18 @@ def algorithmic(cfg, one_launch: bool = False) -> dict:
     else:
         weights_y = N * w_row + 4 * M * N
         ops = 2 * M * N * K
+    if cfg["op"] == "moe":
+        import synth
+        wbytes = len(set(synth.routing(cfg["E"], cfg["top_k"]).tolist())) * N * w_row
+    elif cfg["op"] in ("moe_tokens", "moe_gemm"):
+        wbytes = len(set(ids.reshape(-1).tolist())) * N * w_row
+    else:
+        wbytes = N * w_row
     if one_launch:
-        return {"quant_bytes": 0, "product_bytes": weights_y + quant, "ops": ops}
+        return {"quant_bytes": 0, "product_bytes": weights_y + quant, "ops": ops,
+                "weight_bytes": wbytes}
     prod = weights_y + M * K + 4 * M * (K // 32)
-    return {"quant_bytes": quant, "product_bytes": prod, "ops": ops}
+    return {"quant_bytes": quant, "product_bytes": prod, "ops": ops, "weight_bytes": wbytes}
 
 
 def traffic_from_profiles(workload: str, khash: str = ""):
@@ -111,7 +124,8 @@ def traffic_from_profiles(workload: str, khash: str = ""):
 def cpu_baseline(cfg, budget_s: float = 12.0) -> dict:
     """The CPU oracle on a bounded sample of the workload: the first `rows`
     weight rows (quantized by the oracle, untimed), then timed repetitions of
-    activation quantization + fp64 product until `budget_s` is spent."""
+    activation quantization + fp64 product until `budget_s` is spent (at
+    least 3); the figure is the median repetition."""
     import numpy as np
     import oracle
     import synth
@@ -137,22 +151,24 @@ def cpu_baseline(cfg, budget_s: float = 12.0) -> dict:
     packed = oracle.quantize_weights(W)
     Mb = min(M, 64)
     a = synth.activations(M, K)[:Mb]
-    reps, t0 = 0, time.perf_counter()
+    times, t_all = [], time.perf_counter()
     while True:
+        t0 = time.perf_counter()
         q, d = oracle.quantize_acts(a)
         oracle.ref_gemv(packed, rows, K, q, d)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all >= budget_s and len(times) >= 3:
             break
-    per = el / reps
+    reps = len(times)
+    per = sorted(times)[reps // 2]
     w_row = K // 32 * 10
     sample_bytes = (rows * w_row + Mb * K + 4 * Mb * (K // 32) + 4 * Mb * rows
                     + 4 * Mb * K + Mb * K + 4 * Mb * (K // 32))
     sample_ops = 2 * Mb * rows * K
     out = {"cores": int(blas_threads), "kind": "oracle",
            "sample": f"{rows} weight rows x {Mb} token(s) of {cfg['name']}, "
-                     f"{reps} timed repetitions of quantize_acts + ref_gemv (fp64, numpy); "
+                     f"median of {reps} timed repetitions of quantize_acts + ref_gemv "
+                     f"(fp64, numpy); "
                      + host}
     if cfg["op"] in ("gemm", "gemm_f16"):
         out.update(value=sample_ops / per / 1e12, unit="TOPS")
@@ -161,31 +177,59 @@ def cpu_baseline(cfg, budget_s: float = 12.0) -> dict:
     return out
 
 
-def graph_time_us(launch, steps: int) -> float:
-    """Mean time of launch(i, stream) over back-to-back replays of a HIP graph
-    holding up to 64 consecutive launches (as the products are timed)."""
+def graph_plan(steps: int, ring: int):
+    """Launches per graph (the largest divisor of `steps` up to 64, so that
+    exactly `steps` launches are timed) and graphs in the ring (enough that
+    the ring holds at least `ring` launches, each on its own data slot)."""
+    per_graph = max(g for g in range(1, min(steps, 64) + 1) if steps % g == 0)
+    return per_graph, max(1, -(-ring // per_graph))
+
+
+def capture_ring(launch, per_graph: int, n_graphs: int, stream):
+    """HIP graphs of launch(i, stream): graph g holds i = g * per_graph ..
+    (g + 1) * per_graph - 1."""
+    import torch
+    graphs = []
+    for g in range(n_graphs):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            for i in range(per_graph):
+                launch(g * per_graph + i, stream)
+        graphs.append(gr)
+    return graphs
+
+
+def replay_ring_us(graphs, steps: int, per_graph: int, stream) -> float:
+    """Mean us per launch over exactly `steps` launches: one untimed pass over
+    the whole ring, then the graphs replayed in ring order between HIP events
+    on `stream` (the replays' stream), so each graph's data was last touched
+    a whole ring ago."""
+    import torch
+    for gr in graphs:
+        gr.replay()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for r in range(steps // per_graph):
+        graphs[r % len(graphs)].replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / steps
+
+
+def graph_time_us(launch, steps: int, ring: int = 1) -> float:
+    """Mean time of launch(i, stream) over back-to-back replays of a ring of
+    HIP graphs (as the products are timed); launch i should use data slot
+    i % ring."""
     import torch
     stream = torch.cuda.Stream()
-    per_graph = max(1, min(steps, 64))
+    per_graph, n_graphs = graph_plan(steps, ring)
     with torch.cuda.stream(stream):
         launch(0, stream)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(per_graph):
-                launch(i, stream)
-        g.replay()
-        torch.cuda.synchronize()
-        reps = max(1, steps // per_graph)
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        t1.record(stream)
-        torch.cuda.synchronize()
-        us = t0.elapsed_time(t1) * 1e3 / (reps * per_graph)
-        del g
+        graphs = capture_ring(launch, per_graph, n_graphs, stream)
+        us = replay_ring_us(graphs, steps, per_graph, stream)
+        del graphs
     return us
 
 
@@ -234,11 +278,14 @@ def measure_ceiling(nbytes: int, steps: int, isolated: bool = False) -> dict:
     import bit_gemv_amd as rf
     dev = torch.device("cuda:0")
     nb = max(16, nbytes // 16 * 16)
-    slots = max(2, -(-COLD_BYTES // nb))
-    buf = torch.zeros(slots * nb, dtype=torch.uint8, device=dev)
+    # one slot per launch of the graph ring: a slot is read again only after
+    # the whole ring (>= 1 GiB of other slots)
+    per_graph, n_graphs = graph_plan(steps, max(2, -(-COLD_BYTES // nb)))
+    slots = per_graph * n_graphs
+    buf = torch.zeros(max(slots * nb, COLD_BYTES // 16 * 16), dtype=torch.uint8, device=dev)
     out = torch.empty(rf.READ_CEILING_OUTPUTS, dtype=torch.int32, device=dev)
     us = graph_time_us(lambda i, st: rf.rfp2_read_ceiling(buf[(i % slots) * nb:], nb, out, st),
-                       steps)
+                       steps, slots)
     big = COLD_BYTES // 16 * 16
     us_big = graph_time_us(lambda i, st: rf.rfp2_read_ceiling(buf, big, out, st),
                            min(steps, 64))
@@ -337,7 +384,15 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
             rf.rfp2_quantize_weights(
                 torch.from_numpy(synth.weights(N, K, cfg["sigma"], seed=cfg["wseed"])).to(dev),
                 N, K, master)
-        copies = max(2, -(-COLD_BYTES // per_copy))
+        # one copy per launch of the graph ring; the ring reads >= 1 GiB of
+        # weight bytes (those the steps actually read) before reusing a copy
+        per_graph, n_graphs = graph_plan(steps, max(2, -(-COLD_BYTES // alg["weight_bytes"])))
+        copies = per_graph * n_graphs
+        footprint = copies * alg["weight_bytes"]
+        if footprint < COLD_BYTES:
+            raise RuntimeError(f"{workload}: ring footprint {footprint} B below 1 GiB")
+        if copies * per_copy > MAX_COPY_BYTES:
+            raise RuntimeError(f"{workload}: {copies} weight copies exceed the copy budget")
         bank = [master] + [master.clone() for _ in range(copies - 1)]
         a = torch.from_numpy(synth.activations(M, K)).to(dev)
         q = torch.empty((M, K), dtype=torch.int8, device=dev)
@@ -390,52 +445,28 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
         torch.cuda.synchronize()
         y_eager = y.clone()
 
-        # The timed loops are replayed from HIP graphs: one graph holds
-        # `per_graph` consecutive steps, so neither the host's launch cost nor
-        # the gap between replays sets the pace.  The weights rotate over the
-        # copies inside the graph: a copy comes back only after >= 1 GiB of
-        # other weights, so every step still reads its weights from HBM.
-        per_graph = max(1, min(steps, 64))
-        g_step = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_step, stream=stream):
-            for i in range(per_graph):
-                step(i, stream)
-        g_prod = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_prod, stream=stream):
-            for i in range(per_graph):
-                product(per_graph + i, stream)
+        # The timed loops are replayed from a ring of HIP graphs: graph g holds
+        # the `per_graph` consecutive steps on copies g*per_graph .. + per_graph
+        # - 1, so neither the host's launch cost nor the gap between replays
+        # sets the pace, and a copy comes back only after the whole ring
+        # (>= 1 GiB of other weights): every step reads its weights from HBM.
+        g_step = capture_ring(step, per_graph, n_graphs, stream)
+        g_prod = capture_ring(product, per_graph, n_graphs, stream)
         torch.cuda.synchronize()
         # every replay must reproduce the eager result exactly (all weight
-        # copies are byte-identical)
-        for _ in range(3):
-            y.zero_()
-            torch.cuda.synchronize()
-            g_step.replay()
-            torch.cuda.synchronize()
-            if not torch.equal(y, y_eager):
-                raise RuntimeError(f"{workload}: graph replay differs from the eager step")
+        # copies are byte-identical): the first and the last graph of the ring
+        for gr in {0: g_step[0], 1: g_step[-1]}.values():
+            for _ in range(2):
+                y.zero_()
+                torch.cuda.synchronize()
+                gr.replay()
+                torch.cuda.synchronize()
+                if not torch.equal(y, y_eager):
+                    raise RuntimeError(f"{workload}: graph replay differs from the eager step")
 
-        reps = max(1, steps // per_graph)
-        t_start = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        g_step.replay()
-        t_start.record(stream)
-        for _ in range(reps):
-            g_step.replay()
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        ms_step = t_start.elapsed_time(t_end) / (reps * per_graph)
-
+        ms_step = replay_ring_us(g_step, steps, per_graph, stream) * 1e-3
         # product kernel alone: events around replays of back-to-back launches
-        k_start = torch.cuda.Event(enable_timing=True)
-        k_end = torch.cuda.Event(enable_timing=True)
-        g_prod.replay()
-        k_start.record(stream)
-        for _ in range(reps):
-            g_prod.replay()
-        k_end.record(stream)
-        torch.cuda.synchronize()
-        kern_ms = k_start.elapsed_time(k_end) / (reps * per_graph)
+        kern_ms = replay_ring_us(g_prod, steps, per_graph, stream) * 1e-3
         if not torch.equal(y, y_eager):
             raise RuntimeError(f"{workload}: product graph result differs from the eager step")
         # context only: the same weights every launch, so they stay in the
@@ -458,8 +489,11 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
         kernel = "rfp2_quant_moe_gemv" if cfg["op"] == "moe" else "rfp2_quant_gemv"
     if cfg["op"] in ("gemm", "gemm_f16", "moe_gemm"):
         value = alg["ops"] / (ms_step * 1e-3) / 1e12
-        unit, metric = "TOPS", ("ROCmFP2 prompt-batch MoE GEMM int8 TOPS"
-                                if cfg["op"] == "moe_gemm" else "ROCmFP2 M=512 GEMM int8 TOPS")
+        unit, metric = "TOPS", {
+            "gemm": "ROCmFP2 M=512 GEMM int8 TOPS",
+            "gemm_f16": "ROCmFP2 M=512 GEMM TOPS (int8 x ROCmFP2 product on fp16 matrix cores)",
+            "moe_gemm": "ROCmFP2 prompt-batch MoE GEMM TOPS (int8 x ROCmFP2 product on fp16 "
+                        "matrix cores)"}[cfg["op"]]
         achieved = alg["ops"] / (kern_ms * 1e-3) / 1e12
         # the contraction's own dtype sets the peak: int8 5.0 POP/s, fp16 2.5 PFLOP/s
         peak = I8_PEAK_TOPS if cfg["op"] == "gemm" else F16_PEAK_TFLOPS
@@ -494,11 +528,13 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
     if cfg["op"] in ("moe_tokens", "moe_gemm"):
         config.update(tokens=M, expert_share=cfg["share"])
     config.update(weight_copies=copies, weight_bytes_per_copy=per_copy,
+                  weight_bytes_read_per_step=alg["weight_bytes"],
+                  ring_footprint_bytes=footprint,
                   step=kernel if one else "rfp2_quantize_acts + " + kernel,
-                  graph_steps=per_graph,
+                  graph_steps=per_graph, graphs_in_ring=n_graphs,
                   kernel_hash=khash)
     return {"metric": metric, "value": value, "unit": unit, "ms_per_step": ms_step,
-            "steps": reps * per_graph, "config": config, "roofline": roof, "cfg": cfg}
+            "steps": steps, "config": config, "roofline": roof, "cfg": cfg}
 
 
 def main(argv=None) -> int:
