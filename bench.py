@@ -15,15 +15,17 @@ other weight bytes that the steps actually read (the routed experts only, for
 the MoE workloads), so every step reads its weights from HBM rather than from
 the 256 MB last-level cache.
 
-Timed steps are replayed from a ring of HIP graphs, each holding up to 64
-consecutive steps on its own copies (replays checked bit for bit against an
-eager step), so host launch cost does not set the pace; one untimed pass over
-the whole ring precedes the timed replays.  One JSON line is printed.  `value` is whole-job
+The K timed steps are replayed from one HIP graph (checked bit for bit
+against an eager step) right behind a graph of a few untimed lead-in steps,
+with HIP events on the bench stream between them: the host submits the timed
+graph while the lead-in runs, so neither host launch cost nor the graph's
+start-up enters the figure.  A read of 2 GiB of unrelated memory precedes the
+timed replay.  One JSON line is printed.  `value` is whole-job
 throughput (algorithmic bytes of the step / wall time of the step for GEMV
 workloads, 2*M*N*K / step time for the GEMM workload).  `roofline` describes
-the product kernel alone: HIP events on the bench stream around graph
-replays of back-to-back launches of that kernel (so the average includes the
-gap between consecutive kernels).  For the HBM-bound products it also
+the product kernel alone: HIP events on the bench stream around K
+back-to-back launches of that kernel replayed the same way (so the average
+includes the small gap between consecutive kernels).  For the HBM-bound products it also
 carries `cold_isolated`: 100 single launches, each after a cache flush,
 median and p10 / p90 (see isolated_cold_us), with the plain read timed the
 same way in `ceiling`.
@@ -177,59 +179,75 @@ def cpu_baseline(cfg, budget_s: float = 12.0) -> dict:
     return out
 
 
-def graph_plan(steps: int, ring: int):
-    """Launches per graph (the largest divisor of `steps` up to 64, so that
-    exactly `steps` launches are timed) and graphs in the ring (enough that
-    the ring holds at least `ring` launches, each on its own data slot)."""
-    per_graph = max(g for g in range(1, min(steps, 64) + 1) if steps % g == 0)
-    return per_graph, max(1, -(-ring // per_graph))
+LEAD = 8                       # untimed launches at the head of a timed graph
 
 
-def capture_ring(launch, per_graph: int, n_graphs: int, stream):
-    """HIP graphs of launch(i, stream): graph g holds i = g * per_graph ..
-    (g + 1) * per_graph - 1."""
+def ring_slots(weight_bytes: int) -> int:
+    """Data slots a timed loop rotates through: a slot is read again only
+    after >= 1 GiB of other slots."""
+    return max(2, -(-COLD_BYTES // weight_bytes))
+
+
+def flush_caches(nbytes: int = 2 * COLD_BYTES) -> None:
+    """Read `nbytes` of an unrelated buffer (torch's max): the caches then
+    hold clean lines of nothing the timed launches read."""
     import torch
-    graphs = []
-    for g in range(n_graphs):
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr, stream=stream):
-            for i in range(per_graph):
-                launch(g * per_graph + i, stream)
-        graphs.append(gr)
-    return graphs
-
-
-def replay_ring_us(graphs, steps: int, per_graph: int, stream) -> float:
-    """Mean us per launch over exactly `steps` launches: one untimed pass over
-    the whole ring, then the graphs replayed in ring order between HIP events
-    on `stream` (the replays' stream), so each graph's data was last touched
-    a whole ring ago."""
-    import torch
-    for gr in graphs:
-        gr.replay()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for r in range(steps // per_graph):
-        graphs[r % len(graphs)].replay()
-    t1.record(stream)
+    junk = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    junk.max()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) * 1e3 / steps
+    del junk
+
+
+def timed_graph(launch, steps: int, stream):
+    """Two HIP graphs: LEAD untimed launches launch(0 .. LEAD-1), then the
+    `steps` timed launches launch(LEAD + i).  -> (lead graph, timed graph)."""
+    import torch
+    g_lead = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_lead, stream=stream):
+        for i in range(LEAD):
+            launch(i, stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            launch(LEAD + i, stream)
+    return g_lead, g
+
+
+def replay_timed_us(tg, steps: int, stream) -> float:
+    """Mean us per timed launch of a timed_graph: one untimed replay of both
+    graphs and a cache flush, then the lead graph, the start event, the timed
+    graph and the end event, enqueued back to back on `stream`: the host
+    submits the timed graph while the lead graph still runs, so the events
+    bracket back-to-back kernels rather than the graph's start-up."""
+    import torch
+    g_lead, g = tg
+    with torch.cuda.stream(stream):
+        g_lead.replay()
+        g.replay()
+        torch.cuda.synchronize()
+        flush_caches()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        g_lead.replay()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
 
 
 def graph_time_us(launch, steps: int, ring: int = 1) -> float:
-    """Mean time of launch(i, stream) over back-to-back replays of a ring of
-    HIP graphs (as the products are timed); launch i should use data slot
-    i % ring."""
+    """Mean time of launch(i, stream) over `steps` back-to-back launches
+    timed inside a HIP graph (as the products are timed); launch i should use
+    data slot i % ring."""
     import torch
     stream = torch.cuda.Stream()
-    per_graph, n_graphs = graph_plan(steps, ring)
     with torch.cuda.stream(stream):
         launch(0, stream)
         torch.cuda.synchronize()
-        graphs = capture_ring(launch, per_graph, n_graphs, stream)
-        us = replay_ring_us(graphs, steps, per_graph, stream)
-        del graphs
+        tg = timed_graph(launch, steps, stream)
+        us = replay_timed_us(tg, steps, stream)
+        del tg
     return us
 
 
@@ -278,20 +296,18 @@ def measure_ceiling(nbytes: int, steps: int, isolated: bool = False) -> dict:
     import bit_gemv_amd as rf
     dev = torch.device("cuda:0")
     nb = max(16, nbytes // 16 * 16)
-    # one slot per launch of the graph ring: a slot is read again only after
-    # the whole ring (>= 1 GiB of other slots)
-    per_graph, n_graphs = graph_plan(steps, max(2, -(-COLD_BYTES // nb)))
-    slots = per_graph * n_graphs
-    buf = torch.zeros(max(slots * nb, COLD_BYTES // 16 * 16), dtype=torch.uint8, device=dev)
+    slot = -(-nb // 4096) * 4096             # slices start page-aligned, as allocations do
+    slots = ring_slots(slot)
+    buf = torch.zeros(max(slots * slot, COLD_BYTES // 16 * 16), dtype=torch.uint8, device=dev)
     out = torch.empty(rf.READ_CEILING_OUTPUTS, dtype=torch.int32, device=dev)
-    us = graph_time_us(lambda i, st: rf.rfp2_read_ceiling(buf[(i % slots) * nb:], nb, out, st),
+    us = graph_time_us(lambda i, st: rf.rfp2_read_ceiling(buf[(i % slots) * slot:], nb, out, stream=st),
                        steps, slots)
     big = COLD_BYTES // 16 * 16
-    us_big = graph_time_us(lambda i, st: rf.rfp2_read_ceiling(buf, big, out, st),
-                           min(steps, 64))
+    us_big = graph_time_us(lambda i, st: rf.rfp2_read_ceiling(buf, big, out, stream=st),
+                           min(steps, 16))
     iso = None
     if isolated:
-        iso = isolated_cold_us(lambda st: rf.rfp2_read_ceiling(buf, nb, out, st),
+        iso = isolated_cold_us(lambda st: rf.rfp2_read_ceiling(buf, nb, out, stream=st),
                                torch.cuda.Stream())["median_us"]
     del buf, out
     torch.cuda.empty_cache()
@@ -384,10 +400,9 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
             rf.rfp2_quantize_weights(
                 torch.from_numpy(synth.weights(N, K, cfg["sigma"], seed=cfg["wseed"])).to(dev),
                 N, K, master)
-        # one copy per launch of the graph ring; the ring reads >= 1 GiB of
-        # weight bytes (those the steps actually read) before reusing a copy
-        per_graph, n_graphs = graph_plan(steps, max(2, -(-COLD_BYTES // alg["weight_bytes"])))
-        copies = per_graph * n_graphs
+        # consecutive steps read consecutive copies; a copy comes back only
+        # after >= 1 GiB of the weight bytes the steps actually read
+        copies = ring_slots(alg["weight_bytes"])
         footprint = copies * alg["weight_bytes"]
         if footprint < COLD_BYTES:
             raise RuntimeError(f"{workload}: ring footprint {footprint} B below 1 GiB")
@@ -445,28 +460,27 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
         torch.cuda.synchronize()
         y_eager = y.clone()
 
-        # The timed loops are replayed from a ring of HIP graphs: graph g holds
-        # the `per_graph` consecutive steps on copies g*per_graph .. + per_graph
-        # - 1, so neither the host's launch cost nor the gap between replays
-        # sets the pace, and a copy comes back only after the whole ring
-        # (>= 1 GiB of other weights): every step reads its weights from HBM.
-        g_step = capture_ring(step, per_graph, n_graphs, stream)
-        g_prod = capture_ring(product, per_graph, n_graphs, stream)
+        # The timed loops are HIP graphs (timed_graph): LEAD untimed steps,
+        # then exactly `steps` steps between two event-record nodes, step i on
+        # copy i % copies, replayed after a cache flush, so neither the host's
+        # launch cost nor the graph's start-up enters the figure and every step
+        # reads its weights from HBM.
+        g_step = timed_graph(step, steps, stream)
+        g_prod = timed_graph(product, steps, stream)
         torch.cuda.synchronize()
-        # every replay must reproduce the eager result exactly (all weight
-        # copies are byte-identical): the first and the last graph of the ring
-        for gr in {0: g_step[0], 1: g_step[-1]}.values():
-            for _ in range(2):
-                y.zero_()
-                torch.cuda.synchronize()
-                gr.replay()
-                torch.cuda.synchronize()
-                if not torch.equal(y, y_eager):
-                    raise RuntimeError(f"{workload}: graph replay differs from the eager step")
+        # a replay must reproduce the eager result exactly (all weight copies
+        # are byte-identical)
+        for _ in range(2):
+            y.zero_()
+            torch.cuda.synchronize()
+            g_step[1].replay()
+            torch.cuda.synchronize()
+            if not torch.equal(y, y_eager):
+                raise RuntimeError(f"{workload}: graph replay differs from the eager step")
 
-        ms_step = replay_ring_us(g_step, steps, per_graph, stream) * 1e-3
-        # product kernel alone: events around replays of back-to-back launches
-        kern_ms = replay_ring_us(g_prod, steps, per_graph, stream) * 1e-3
+        ms_step = replay_timed_us(g_step, steps, stream) * 1e-3
+        # product kernel alone: events around back-to-back launches of it
+        kern_ms = replay_timed_us(g_prod, steps, stream) * 1e-3
         if not torch.equal(y, y_eager):
             raise RuntimeError(f"{workload}: product graph result differs from the eager step")
         # context only: the same weights every launch, so they stay in the
@@ -531,7 +545,7 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
                   weight_bytes_read_per_step=alg["weight_bytes"],
                   ring_footprint_bytes=footprint,
                   step=kernel if one else "rfp2_quantize_acts + " + kernel,
-                  graph_steps=per_graph, graphs_in_ring=n_graphs,
+                  timed_graph=f"{LEAD} untimed + {steps} timed steps",
                   kernel_hash=khash)
     return {"metric": metric, "value": value, "unit": unit, "ms_per_step": ms_step,
             "steps": steps, "config": config, "roofline": roof, "cfg": cfg}

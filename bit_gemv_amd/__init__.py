@@ -44,7 +44,7 @@ _SIGNATURES = {
                        _c_p, _c_p, ctypes.c_size_t, _c_p], ctypes.c_int),
     "rfp2_moe_gemm_noalloc": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_i64, _c_p, _c_p,
                                _c_p, _c_p, _c_p], ctypes.c_int),
-    "rfp2_read_ceiling": ([_c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
+    "rfp2_read_ceiling": ([_c_p, _c_i64, ctypes.c_uint32, _c_p, _c_p], ctypes.c_int),
     "rfp2_quant_gemv": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p], ctypes.c_int),
     "rfp2_quant_moe_gemv": ([_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p,
                              _c_p, _c_p, _c_p], ctypes.c_int),
@@ -228,7 +228,7 @@ def rfp2_moe_gemm(w, E: int, N: int, K: int, ids, T: int, top_k: int, q, d, y, e
         _ptr(workspace, torch.uint8, need, "workspace"), workspace.numel(), _stream(stream)))
 
 
-READ_CEILING_OUTPUTS = 2048
+READ_CEILING_OUTPUTS = 524288
 
 
 MOE_GEMM_NOALLOC_MAX_BYTES = 1 << 20
@@ -245,13 +245,18 @@ def rfp2_moe_gemm_noalloc(w, E: int, N: int, K: int, ids, T: int, top_k: int, q,
         _ptr(y, torch.float32, T * top_k * N, "y"), errp, _stream(stream)))
 
 
-def rfp2_read_ceiling(buf, nbytes: int, out, stream=None) -> None:
-    """Measurement helper: read nbytes of buf with plain 16-byte loads."""
+def read_ceiling_threads(nbytes: int) -> int:
+    """Threads of the read helper's grid for nbytes (256 per workgroup)."""
+    return 256 * min(2048, max(1, -(-(nbytes // 16) // 256)))
+
+
+def rfp2_read_ceiling(buf, nbytes: int, out, magic: int = 0x9E3779B9, stream=None) -> None:
+    """Measurement helper: read nbytes of buf with plain 16-byte loads; a
+    thread whose XOR of what it read equals `magic` writes it to out[thread]."""
     import torch
     _check("rfp2_read_ceiling", lib().rfp2_read_ceiling(
-        _ptr(buf, torch.uint8, nbytes, "buf"), nbytes,
-        _ptr(out, torch.int32, min(READ_CEILING_OUTPUTS, -(-nbytes // 4096)), "out"),
-        _stream(stream)))
+        _ptr(buf, torch.uint8, nbytes, "buf"), nbytes, int(magic) & 0xFFFFFFFF,
+        _ptr(out, torch.int32, read_ceiling_threads(nbytes), "out"), _stream(stream)))
 
 
 def rfp2_quant_gemv(w, N: int, K: int, a, q, d, y, stream=None) -> None:

@@ -198,13 +198,13 @@ rfp2_status rfp2_moe_gemm_noalloc(const uint8_t* w, int64_t E, int64_t N, int64_
       rfp2::launch_moe_gemm_noalloc(w, E, N, K, ids, T, top_k, q, d, y, err, stream));
 }
 
-rfp2_status rfp2_read_ceiling(const uint8_t* buf, int64_t bytes, uint32_t* out,
+rfp2_status rfp2_read_ceiling(const uint8_t* buf, int64_t bytes, uint32_t magic, uint32_t* out,
                               hipStream_t stream) {
   if (!buf || !out) return RFP2_E_NULL;
   if (bytes < 16 || bytes % 16 != 0) return RFP2_E_SHAPE;
   if (!aligned(buf, 16) || !aligned(out, 4)) return RFP2_E_ALIGN;
   (void)hipGetLastError();
-  return from_hip(rfp2::launch_read_ceiling(buf, bytes, out, stream));
+  return from_hip(rfp2::launch_read_ceiling(buf, bytes, magic, out, stream));
 }
 
 rfp2_status rfp2_quant_gemv(const uint8_t* w, int64_t N, int64_t K, const float* a,

@@ -11,7 +11,7 @@ namespace rfp2 {
 
 constexpr int64_t kMaxGrid = 1 << 20;   // workgroups per launch (grid-stride beyond)
 constexpr int kMaxSortExperts = 2048;   // experts of a grouped (sorted) routed product
-constexpr int kReadCeilingGrid = 2048;  // workgroups (and outputs) of the read helper
+constexpr int kReadCeilingGrid = 2048;  // workgroups of the read helper (256 threads each)
 constexpr size_t kNoallocScratchBytes = size_t(1) << 20;  // library-owned workspace per GPU
 
 hipError_t launch_quantize_acts(const float* a, int64_t M, int64_t K, int8_t* q,
@@ -57,7 +57,7 @@ hipError_t launch_moe_gemm_noalloc(const uint8_t* w, int64_t E, int64_t N, int64
                                    const int32_t* ids, int64_t T, int64_t top_k,
                                    const int8_t* q, const float* d, float* y, int32_t* err,
                                    hipStream_t stream);
-hipError_t launch_read_ceiling(const uint8_t* buf, int64_t bytes, uint32_t* out,
+hipError_t launch_read_ceiling(const uint8_t* buf, int64_t bytes, uint32_t magic, uint32_t* out,
                                hipStream_t stream);
 hipError_t launch_debug_decode(const uint8_t* w, int64_t N, int64_t K,
                                int8_t* codes, float* scales, hipStream_t stream);

@@ -303,18 +303,20 @@ rfp2_status rfp2_quant_moe_gemv(const uint8_t* w, int64_t E, int64_t N, int64_t 
 
 /*
  * rfp2_read_ceiling -- measurement helper, not part of the method: reads
- * `bytes` bytes of buf once with the plainest coalesced 16-byte loads (each
- * thread XORs what it reads) and writes one XOR word per workgroup to out.
- * Its time is the ceiling for any kernel that must read that many bytes
- * (launch and ramp-up included), the yardstick the products' effective
- * bandwidth is reported against besides the HBM peak.
+ * `bytes` bytes of buf once with the plainest coalesced 16-byte loads
+ * (thread t of the grid reads pieces t, t + T, t + 2T, ... of 16 bytes,
+ * T = 256 * min(2048, ceil(bytes / 4096)) threads) and XORs the four words of
+ * every piece it reads; a thread whose XOR equals `magic` writes it to
+ * out[t], no other thread writes.  Its time is the ceiling for any kernel that
+ * must read that many bytes (launch and ramp-up included), the yardstick the
+ * products' effective bandwidth is reported against besides the HBM peak.
  *   buf  device bytes, 16-byte aligned.
- *   out  device uint32 [min(2048, ceil(bytes / 4096))] (RFP2_READ_CEILING_OUTPUTS
- *        at most); overwritten.
+ *   out  device uint32 [T] (RFP2_READ_CEILING_OUTPUTS at most); only the
+ *        entries of threads whose XOR equals magic are written.
  * Requires bytes >= 16, bytes % 16 == 0.
  */
-#define RFP2_READ_CEILING_OUTPUTS 2048
-rfp2_status rfp2_read_ceiling(const uint8_t* buf, int64_t bytes, uint32_t* out,
+#define RFP2_READ_CEILING_OUTPUTS 524288
+rfp2_status rfp2_read_ceiling(const uint8_t* buf, int64_t bytes, uint32_t magic, uint32_t* out,
                               hipStream_t stream);
 
 /*

@@ -53,7 +53,7 @@ int main(void) {
   expect("quant_gemv", rfp2_quant_gemv(p, N_, K_, NULL, p, p, p, st), RFP2_E_NULL);
   expect("quant_moe_gemv",
          rfp2_quant_moe_gemv(p, 2, N_, K_, p, 1, p, p, p, NULL, NULL, st), RFP2_E_NULL);
-  expect("read_ceiling", rfp2_read_ceiling(NULL, 16, p, st), RFP2_E_NULL);
+  expect("read_ceiling", rfp2_read_ceiling(NULL, 16, 0u, p, st), RFP2_E_NULL);
   expect("debug_decode", rfp2_debug_decode(p, N_, K_, NULL, p, st), RFP2_E_NULL);
   expect("debug_half_dots", rfp2_debug_half_dots(p, N_, K_, p, 1, NULL, st), RFP2_E_NULL);
   expect("debug_decode_f16", rfp2_debug_decode_f16(p, N_, K_, 0, NULL, st), RFP2_E_NULL);

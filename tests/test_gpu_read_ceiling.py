@@ -1,7 +1,10 @@
-"""The read-ceiling measurement helper really reads every byte it is given:
-the XOR of its per-workgroup words equals the XOR of all 32-bit words of the
-buffer (exact integer check), for sizes with a ragged last pass and sizes
-that need several grid-stride passes."""
+"""The read-ceiling measurement helper really reads every piece it is given:
+in a zero buffer, pieces planted with one value V are each the only non-zero
+piece their thread visits, so exactly the threads that own them (thread
+p mod T for piece p, T threads in the grid-stride grid) find XOR == magic and
+write; every other entry stays untouched.  The planted pieces include the
+first and the last piece, a piece in the ragged last pass, and one per
+grid-stride pass."""
 import numpy as np
 import pytest
 
@@ -12,17 +15,36 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("nbytes", [16, 4096, 1_000_000, 16 * 2048 * 256 * 3 + 48])
-def test_read_ceiling_reads_every_word(nbytes):
+def test_read_ceiling_reads_every_planted_piece(nbytes):
     announce("read_ceiling", nbytes)
-    data = np.random.default_rng(nbytes).integers(0, 256, nbytes + 64, dtype=np.uint8)
-    buf = to_dev(data)
+    pieces = nbytes // 16
+    T = rf.read_ceiling_threads(nbytes)
+    rng = np.random.default_rng(nbytes)
+    passes = -(-pieces // T)
+    # one piece per grid-stride pass, each owned by a distinct thread, plus the
+    # first and the last piece
+    owners = {}
+    for p in [0, pieces - 1] + [int(rng.integers(k * T, min((k + 1) * T, pieces)))
+                                for k in range(passes)]:
+        owners.setdefault(p % T, p)          # one planted piece per thread
+    planted = sorted(owners.values())
+    assert 0 in planted and pieces - 1 in planted
+    data = np.zeros(nbytes + 64, dtype=np.uint8)
+    V = np.array([0x11223344, 0x0A0B0C0D, 0x55667788, 0x01020304], dtype=np.uint32)
+    magic = int(np.bitwise_xor.reduce(V))
+    for p in planted:
+        data[16 * p:16 * p + 16] = V.view(np.uint8)
     out = empty(rf.READ_CEILING_OUTPUTS, torch.int32)
-    out.fill_(0)
-    rf.rfp2_read_ceiling(buf, nbytes, out)
-    grid = min(rf.READ_CEILING_OUTPUTS, -(-(nbytes // 16) // 256))
-    got = np.bitwise_xor.reduce(host(out)[:grid].view(np.uint32))
-    want = np.bitwise_xor.reduce(data[:nbytes].view(np.uint32))
-    assert got == want
+    out.fill_(-1)
+    rf.rfp2_read_ceiling(to_dev(data), nbytes, out, magic=magic)
+    got = host(out)[:T].view(np.uint32)
+    written = np.flatnonzero(got != 0xFFFFFFFF)
+    assert sorted(written.tolist()) == sorted(p % T for p in planted)
+    assert (got[written] == magic).all()
+    # a magic nothing matches: no thread writes
+    out.fill_(-1)
+    rf.rfp2_read_ceiling(to_dev(data), nbytes, out, magic=magic ^ 1)
+    assert (host(out)[:T].view(np.uint32) == 0xFFFFFFFF).all()
 
 
 def test_read_ceiling_rejects_bad_sizes():
