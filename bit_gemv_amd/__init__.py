@@ -51,6 +51,7 @@ _SIGNATURES = {
     "rfp2_debug_decode": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p], ctypes.c_int),
     "rfp2_debug_half_dots": ([_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
     "rfp2_debug_decode_f16": ([_c_p, _c_i64, _c_i64, ctypes.c_int, _c_p, _c_p], ctypes.c_int),
+    "rfp2_debug_decode_i8": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p], ctypes.c_int),
 }
 
 
@@ -302,3 +303,11 @@ def rfp2_debug_decode_f16(w, N: int, K: int, form: int, h_out, stream=None) -> N
     _check("rfp2_debug_decode_f16", lib().rfp2_debug_decode_f16(
         _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), N, K, int(form),
         _ptr(h_out, torch.int16, N * K, "h_out"), _stream(stream)))
+
+
+def rfp2_debug_decode_i8(w, N: int, K: int, codes_out, scales_out, stream=None) -> None:
+    import torch
+    _check("rfp2_debug_decode_i8", lib().rfp2_debug_decode_i8(
+        _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), N, K,
+        _ptr(codes_out, torch.int8, N * K, "codes_out"),
+        _ptr(scales_out, torch.float32, N * K // 16, "scales_out"), _stream(stream)))

@@ -216,7 +216,64 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(
     }
 }
 
+// Inspection of the GEMM's decode (rfp2_debug_decode_i8): the two blocks of
+// pair p of the flat block stream, loaded and decoded exactly as
+// stage_to_lds decodes a thread's pair (the second block funnel-shifted out
+// of the dwords), written in natural weight order.
+__global__ __launch_bounds__(256) void debug_decode_i8_kernel(
+    const uint8_t* __restrict__ w, int64_t nblocks, uint32_t* __restrict__ codes,
+    float* __restrict__ scales) {
+  const float fix = scale_fix();
+  for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < (nblocks + 1) / 2;
+       p += (int64_t)gridDim.x * 256) {
+    // the 20-byte pair as 16-bit pieces (the stream is only 2-byte aligned
+    // here); bytes past the end read as zero
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(w + p * 20);
+    const int64_t end = nblocks * 10;
+    Prefetch f;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int64_t off = p * 20 + 4 * i;
+      f.wd[i] = (off < end ? (uint32_t)src[2 * i] : 0u) |
+                ((off + 2 < end ? (uint32_t)src[2 * i + 1] : 0u) << 16);
+    }
+    const uint32_t cw[4] = {f.wd[0], f.wd[1], __builtin_amdgcn_alignbit(f.wd[3], f.wd[2], 16),
+                            __builtin_amdgcn_alignbit(f.wd[4], f.wd[3], 16)};
+    const float nan = __builtin_nanf("");
+    const bool bad0 = scale_flags_set<0>(scale_pair_bad<0>(f.wd[2]));
+    const bool bad1 = scale_flags_set<1>(scale_pair_bad<1>(f.wd[4]));
+    const float sv[4] = {bad0 ? nan : fp8_byte<0>(f.wd[2]) * fix,
+                         bad0 ? nan : fp8_byte<1>(f.wd[2]) * fix,
+                         bad1 ? nan : fp8_byte<2>(f.wd[4]) * fix,
+                         bad1 ? nan : fp8_byte<3>(f.wd[4]) * fix};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {              // the four halves of the pair
+      const int64_t blk = 2 * p + (h >> 1);
+      if (blk >= nblocks) break;
+      uint32_t W[4];
+      expand_half(cw[h], W);
+      // weight 4j+i of the half is byte j of W[i]
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = __builtin_amdgcn_perm(W[1], W[0], 0x00000400u + 0x0101u * j);
+        const uint32_t hi = __builtin_amdgcn_perm(W[3], W[2], 0x00000400u + 0x0101u * j);
+        codes[blk * 8 + (h & 1) * 4 + j] = (lo & 0xFFFFu) | (hi << 16);
+      }
+      scales[blk * 2 + (h & 1)] = sv[h];
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_debug_decode_i8(const uint8_t* w, int64_t N, int64_t K, int8_t* codes,
+                                  float* scales, hipStream_t stream) {
+  const int64_t npairs = (N * (K / 32) + 1) / 2;
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((npairs + 255) / 256, kMaxGrid));
+  hipLaunchKernelGGL(debug_decode_i8_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, w,
+                     N * (K / 32), reinterpret_cast<uint32_t*>(codes), scales);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
                        const float* d, int64_t M, float* y, hipStream_t stream) {

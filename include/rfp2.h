@@ -356,6 +356,19 @@ rfp2_status rfp2_debug_half_dots(const uint8_t* w, int64_t N, int64_t K,
 rfp2_status rfp2_debug_decode_f16(const uint8_t* w, int64_t N, int64_t K, int form,
                                   uint16_t* h_out, hipStream_t stream);
 
+/*
+ * rfp2_debug_decode_i8: the decode of rfp2_gemm (the int8 matrix-core
+ * product): blocks taken in dword-aligned 20-byte pairs, as a GEMM thread
+ * loads them (the second block of a pair starts at byte 2 of a dword), each
+ * half expanded to its int8 lanes and its scale converted as the GEMM stages
+ * them.  codes_out [N][K] int8 and scales_out [N][K/16] fp32 as
+ * rfp2_debug_decode (NaN for both scales of a block with an illegal byte).
+ * Requires N >= 1, K >= 32, K % 32 == 0; w 2-byte aligned, the outputs
+ * 4-byte aligned.
+ */
+rfp2_status rfp2_debug_decode_i8(const uint8_t* w, int64_t N, int64_t K, int8_t* codes_out,
+                                 float* scales_out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -156,3 +156,22 @@ def test_f16_decode_bitexact(form, N, K):
     bad = np.repeat(bad_blk, 32, axis=1)
     assert np.isnan(got[bad]).all()
     assert np.array_equal(got[~bad].view(np.uint16), ref[~bad].view(np.uint16))
+
+
+@pytest.mark.parametrize("N,K", [(16, 1024), (3, 96), (5, 32)])
+def test_gemm_i8_decode_bitexact_both_blocks_of_a_pair(N, K):
+    # the int8 GEMM's staging decode (pairs of blocks, the second one
+    # funnel-shifted), bit for bit: every code byte and every scale byte in
+    # both blocks of a pair; an illegal byte makes both scales of its block NaN
+    announce("debug_decode_i8", N, K)
+    flat = parity_blocks(256)
+    packed = np.resize(flat, N * K // 32 * 10).reshape(N, K // 32 * 10)
+    codes, scales = empty((N, K), torch.int8), empty((N, K // 16), torch.float32)
+    rf.rfp2_debug_decode_i8(to_dev(packed.reshape(-1)), N, K, codes, scales)
+    codes, scales = host(codes), host(scales)
+    assert np.array_equal(codes, oracle.decoded_int8(packed, N, K))
+    _, eb = oracle.unpack_matrix(packed, N, K)
+    ref = _expected_scales(eb)
+    bad_blk = np.repeat(np.isnan(ref).reshape(N, -1, 2).any(axis=2), 2, axis=1)
+    assert np.isnan(scales[bad_blk]).all()
+    assert np.array_equal(scales[~bad_blk], ref[~bad_blk])
