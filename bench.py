@@ -55,7 +55,10 @@ SECONDARY = ["gemv_512x2048", "gemv_4096x4096", "moe_128x1536x4096_top8",
              "gemm_f16_512x14336x4096", "moe_gemm_128x1536x4096_top8_t512"]
 MAX_COPY_BYTES = 40 << 30      # device memory the weight copies may take
 KERNEL_SOURCES = ["rfp2_device.h", "gemv_kernel.h", "gemv.hip", "gemv_moe.hip", "gemm.hip",
-                  "gemm_f16.hip", "moe_sort.hip", "quantize.hip"]
+                  "gemm_f16.hip", "f16_decode.h", "moe_sort.hip", "quantize.hip"]
+# the sources of the GEMV kernels (one-token, multi-column and routed forms):
+# a counter record taken on them stays valid while these are unchanged
+GEMV_SOURCES = ["rfp2_device.h", "gemv_kernel.h", "gemv.hip", "gemv_moe.hip", "gemv_m34.hip"]
 
 
 def kernel_hash(sources=None) -> str:
@@ -108,19 +111,19 @@ def algorithmic(cfg, one_launch: bool = False) -> dict:
     return {"quant_bytes": quant, "product_bytes": prod, "ops": ops, "weight_bytes": wbytes}
 
 
-def traffic_from_profiles(workload: str, khash: str = ""):
+def traffic_from_profiles(workload: str):
     """HBM bytes per launch of the product kernel, from the committed counter
-    summary, if it was taken on the current sources of that kernel (the
-    record names the files its hash covers)."""
+    summary, if it was taken on the current sources of the GEMV kernels."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
-            rec = json.load(f).get(workload)
+            rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_hash") != kernel_hash(rec.get("hash_sources")):
+    if rec.get("kernel_hash") != kernel_hash(rec.get("hash_sources")):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    w = rec.get("workloads", {}).get(workload)
+    return w.get("hbm_bytes_per_launch") if w else None
 
 
 def cpu_baseline(cfg, budget_s: float = 12.0) -> dict:
@@ -519,7 +522,7 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
         achieved = alg["product_bytes"] / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS}
-    roof.update(traffic=traffic_from_profiles(workload, khash), kernel=kernel,
+    roof.update(traffic=traffic_from_profiles(workload), kernel=kernel,
                 kernel_us=kern_ms * 1e3, algorithmic_bytes=alg["product_bytes"],
                 algorithmic_ops=alg["ops"])
     if warm_us is not None:
