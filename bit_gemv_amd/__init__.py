@@ -50,6 +50,7 @@ _SIGNATURES = {
                              _c_p, _c_p, _c_p], ctypes.c_int),
     "rfp2_debug_decode": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p], ctypes.c_int),
     "rfp2_debug_half_dots": ([_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
+    "rfp2_debug_half_sums_mf": ([_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
     "rfp2_debug_decode_f16": ([_c_p, _c_i64, _c_i64, ctypes.c_int, _c_p, _c_p], ctypes.c_int),
     "rfp2_debug_decode_i8": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p], ctypes.c_int),
 }
@@ -292,6 +293,14 @@ def rfp2_debug_decode(w, N: int, K: int, codes_out, scales_out, stream=None) -> 
 def rfp2_debug_half_dots(w, N: int, K: int, q, M: int, sums_out, stream=None) -> None:
     import torch
     _check("rfp2_debug_half_dots", lib().rfp2_debug_half_dots(
+        _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), N, K,
+        _ptr(q, torch.int8, M * K, "q"), M,
+        _ptr(sums_out, torch.int32, M * N * _blocks(K) * 2, "sums_out"), _stream(stream)))
+
+
+def rfp2_debug_half_sums_mf(w, N: int, K: int, q, M: int, sums_out, stream=None) -> None:
+    import torch
+    _check("rfp2_debug_half_sums_mf", lib().rfp2_debug_half_sums_mf(
         _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), N, K,
         _ptr(q, torch.int8, M * K, "q"), M,
         _ptr(sums_out, torch.int32, M * N * _blocks(K) * 2, "sums_out"), _stream(stream)))

@@ -13,6 +13,10 @@
 //     at byte 2 of a dword, the packed fp8 convert of both scales) and summed
 //     by block_half_sums against activations transposed as the GEMV stages
 //     them.
+//   * GEMV matrix-core half sums (rfp2_debug_half_sums_mf): the same blocks
+//     summed by half_sums_mf, the 4x4x4 int8 matrix-core form of two to four
+//     columns, with its lane layout: quads of lanes are four rows at one
+//     group, each lane supplies one column's activations.
 //   * fp16 decode (rfp2_debug_decode_f16): pairs of blocks, as the fp16
 //     matrix-core kernels load them, decoded by decode_pair_block_f16 (the
 //     dense prompt-batch kernel) or decode_half (the routed kernel).
@@ -26,6 +30,8 @@ namespace {
 
 using gemv_detail::block_half_sums;
 using gemv_detail::decode_block;
+using gemv_detail::half_sums_mf;
+using gemv_detail::v4i;
 
 // `n` dwords of the block stream starting at byte `off` (a multiple of 2),
 // read as 16-bit pieces (the stream is only 2-byte aligned here); bytes at or
@@ -116,6 +122,62 @@ __global__ __launch_bounds__(256) void debug_half_dots_kernel(
   }
 }
 
+// Quads of four rows at one 8-block group (rows 4r..4r+3 of the matrix,
+// group g of each row) against quads of four columns (4c..4c+3), the lane
+// layout of the GEMV's matrix-core form: lane 4u+i of a wave holds row 4r+i
+// of quad u as the B operand and column 4c+i as the A operand, and receives
+// its row's sums for columns 4c..4c+3.  Sixteen quads per wave and
+// iteration; every lane runs every iteration (a quad past the end recomputes
+// the last one, and a row or column past the end re-reads the last one;
+// neither stores).  Requires nb % 8 == 0.
+__global__ __launch_bounds__(256) void debug_half_sums_mf_kernel(
+    const uint8_t* __restrict__ w, int64_t N, int64_t nb, const uint32_t* __restrict__ q,
+    int64_t M, int32_t* __restrict__ sums) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 3;
+  const int64_t row_quads = (N + 3) / 4, col_quads = (M + 3) / 4, groups = nb / 8;
+  const int64_t nquads = col_quads * row_quads * groups;
+  const int64_t waves = (int64_t)gridDim.x * 4;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  for (int64_t base = wave * 16; base < nquads; base += waves * 16) {   // uniform per wave
+    const int64_t mine = base + (lane >> 2);
+    const bool store = mine < nquads;
+    const int64_t Q = store ? mine : nquads - 1;
+    const int64_t g = Q % groups, rest = Q / groups;
+    const int64_t r4 = rest % row_quads, c4 = rest / row_quads;
+    const int64_t n = 4 * r4 + i;
+    const int64_t nr = n < N ? n : N - 1;
+    const int64_t ma = 4 * c4 + i < M ? 4 * c4 + i : M - 1;
+    uint32_t dw[20];
+    load_dwords(w, (nr * nb + 8 * g) * 10, N * nb * 10, dw);
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) {
+      const int64_t b = 8 * g + jb;
+      uint32_t W0[4], W1[4], sc;
+      float s0, s1;
+      decode_block(dw, jb, W0, W1, s0, s1, sc);
+      const uint32_t* qa = q + (ma * nb + b) * 8;
+      const uint32_t X0[4] = {qa[0], qa[1], qa[2], qa[3]};
+      const uint32_t X1[4] = {qa[4], qa[5], qa[6], qa[7]};
+      uint32_t T0[4], T1[4];
+      transpose_half(X0, T0);
+      transpose_half(X1, T1);
+      const v4i S0 = half_sums_mf(W0, make_uint4(T0[0], T0[1], T0[2], T0[3]));
+      const v4i S1 = half_sums_mf(W1, make_uint4(T1[0], T1[1], T1[2], T1[3]));
+      if (store && n < N) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t m = 4 * c4 + j;
+          if (m < M) {
+            sums[((m * N + n) * nb + b) * 2 + 0] = S0[j];
+            sums[((m * N + n) * nb + b) * 2 + 1] = S1[j];
+          }
+        }
+      }
+    }
+  }
+}
+
 // k order of expand_half_f16's 16 fp16 values (position e holds weight
 // kOrder[e] of the half).
 __device__ __forceinline__ int f16_weight_of(int e) {
@@ -190,6 +252,17 @@ hipError_t launch_debug_half_dots(const uint8_t* w, int64_t N, int64_t K,
   hipLaunchKernelGGL(debug_half_dots_kernel, dim3((uint32_t)grid_for(M * ((nblocks + 7) / 8))),
                      dim3(256), 0, stream, w, nblocks, nb,
                      reinterpret_cast<const uint32_t*>(q), M, sums);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_half_sums_mf(const uint8_t* w, int64_t N, int64_t K,
+                                     const int8_t* q, int64_t M, int32_t* sums,
+                                     hipStream_t stream) {
+  const int64_t nb = K / 32;
+  const int64_t quads = ((M + 3) / 4) * ((N + 3) / 4) * (nb / 8);
+  // 64 quads per 256-thread workgroup and iteration
+  hipLaunchKernelGGL(debug_half_sums_mf_kernel, dim3((uint32_t)grid_for(quads * 4)), dim3(256),
+                     0, stream, w, N, nb, reinterpret_cast<const uint32_t*>(q), M, sums);
   return hipGetLastError();
 }
 

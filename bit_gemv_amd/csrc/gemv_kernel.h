@@ -159,6 +159,66 @@ __device__ __forceinline__ void group_product(const uint32_t (&dw)[20],
   }
 }
 
+// Matrix-core form of group_product for two to four columns.  The int32 half
+// sums come from v_mfma_i32_4x4x4_16b_i8 instead of the lane's own dot4
+// chains: the instruction is sixteen independent 4x4x4 products, one per
+// quad of lanes (lanes 4q..4q+3); in quad q, lane 4q+i supplies row i of A
+// (four int8 along k) and lane 4q+j column j of B, and lane 4q+j receives
+// D[i][j] in its register i.  Here the four lanes of a quad are four weight
+// rows at the same group, B is each lane's own expanded weight word, and A
+// is column i's activation word (lane 4q+i reads column i), so lane 4q+j
+// gets its own row's sums for all four columns, one per register.  Four
+// steps over the words i = 0..3 of a half (weights i, 4+i, 8+i, 12+i, the
+// activations transposed to match) accumulate the half's int32 sum: the
+// same integers as half_dot, so the outputs are bit for bit those of
+// group_product.  `act` points at this lane's column's activations of the
+// group, `dact` at the group's block scales laid out [block][column] with
+// four columns per block.  Column slots past M (M < 4) compute unused sums.
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4i half_sums_mf(const uint32_t (&W)[4], const uint4& A) {
+  v4i s = __builtin_amdgcn_mfma_i32_4x4x4i8((int)A.x, (int)W[0], v4i{0, 0, 0, 0}, 0, 0, 0);
+  s = __builtin_amdgcn_mfma_i32_4x4x4i8((int)A.y, (int)W[1], s, 0, 0, 0);
+  s = __builtin_amdgcn_mfma_i32_4x4x4i8((int)A.z, (int)W[2], s, 0, 0, 0);
+  s = __builtin_amdgcn_mfma_i32_4x4x4i8((int)A.w, (int)W[3], s, 0, 0, 0);
+  return s;
+}
+
+template <int M>
+__device__ __forceinline__ void group_product_mf(const uint32_t (&dw)[20], const uint32_t* act,
+                                                 const float* dact, float (&acc)[M],
+                                                 uint32_t& bad_lo, uint32_t& bad_hi) {
+  static_assert(M >= 2 && M <= 4, "one quad of columns");
+  auto load = [&](int jb, uint4& A0, uint4& A1, float4& d4) {
+    A0 = *reinterpret_cast<const uint4*>(act + jb * 8);
+    A1 = *reinterpret_cast<const uint4*>(act + jb * 8 + 4);
+    d4 = *reinterpret_cast<const float4*>(dact + jb * 4);
+  };
+  // a block's activations are read one block ahead of its products
+  uint4 nA0, nA1;
+  float4 nd;
+  load(0, nA0, nA1, nd);
+#pragma unroll
+  for (int jb = 0; jb < 8; ++jb) {
+    const uint4 A0 = nA0, A1 = nA1;
+    const float4 d4 = nd;
+    if (jb < 7) load(jb + 1, nA0, nA1, nd);
+    uint32_t W0[4], W1[4], sc;
+    float s0, s1;
+    decode_block(dw, jb, W0, W1, s0, s1, sc);
+    if ((jb & 1) == 0)
+      bad_lo |= sc;
+    else
+      bad_hi |= sc;
+    const v4i S0 = half_sums_mf(W0, A0);
+    const v4i S1 = half_sums_mf(W1, A1);
+    const float dm[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      acc[m] = fmaf(dm[m], fmaf(s1, (float)S1[m], s0 * (float)S0[m]), acc[m]);
+  }
+}
+
 // A wave's chunk of weights is its S = 64/L rows x L consecutive groups
 // (80*L bytes per row) = 320 16-byte pieces, fetched with fully coalesced
 // direct-to-LDS loads (global_load_lds_dwordx4: lane l of instruction k
@@ -379,6 +439,21 @@ __device__ __forceinline__ float row_sum(float v, int L) {
   return v;
 }
 
+// The same for the matrix-core lane order, where the L lanes of a row are 4
+// apart (lane bits 2 .. 2 + log2 L): the sum lands in the row's lane t = 0
+// (the other lanes hold partial sums).  Row shifts by 4 and 8 inside each
+// 16-lane row, then lane shuffles; each step adds the partner group that
+// lies above, so the summation tree is row_sum's.
+__device__ __forceinline__ float row_sum_mf(float v, int L) {
+  if (L >= 2) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x104,
+                                                               0xF, 0xF, false));  // row_shl:4
+  if (L >= 4) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x108,
+                                                               0xF, 0xF, false));  // row_shl:8
+  if (L >= 8) v += __shfl_down(v, 16, 64);
+  if (L >= 16) v += __shfl_down(v, 32, 64);
+  return v;
+}
+
 // Wait until at most 5*ahead loads (= `ahead` chunks) are outstanding.
 __device__ __forceinline__ void wait_chunks(int ahead) {
   switch (ahead) {
@@ -400,20 +475,26 @@ __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)"
 // groups, so no workgroup barrier precedes the products; one barrier
 // precedes the final cross-wave sum.  M activation columns; MOE selects the
 // weight matrix through ids[blockIdx.y].  QH > 0: the quantizing form, each
-// lane quantizing QH (1 or 2) halves of the wave's activation slice.
-template <int M, int JT, bool MOE, int QH>
+// lane quantizing QH (1 or 2) halves of the wave's activation slice.  MF:
+// the matrix-core form of two to four columns (group_product_mf), in which
+// the four lanes of a quad are four rows at the same group: lane =
+// (slot / 4) * 4L + t * 4 + slot % 4, so it needs L <= 16.  A routed group
+// with fewer columns than M computes the missing ones from a repeat of its
+// last column and does not store them.
+template <int M, int JT, bool MOE, int QH, bool MF = false>
 __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
   constexpr bool QA = QH > 0;
   static_assert(QH >= 0 && QH <= 2, "one or two halves per lane");
   static_assert(!QA || (M == 1 && JT == 1), "the quantizing form is one column, one chunk");
+  static_assert(!MF || (M >= 2 && M <= 4 && !QA), "matrix-core form: 2..4 columns");
   extern __shared__ uint32_t lds[];
   const int K = p.K, N = p.N;
   const int ls = p.lshift;
   const int L = 1 << ls;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int slot = lane >> ls;
-  const int t = lane & (L - 1);
+  const int slot = MF ? (lane & 3) | ((lane >> (2 + ls)) << 2) : lane >> ls;
+  const int t = MF ? (lane >> 2) & (L - 1) : lane & (L - 1);
   const int row0 = blockIdx.x * (64 >> ls);
   const int row = row0 + slot;
   const int row_bytes = (K >> 8) * 80;
@@ -467,14 +548,15 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
   // their block scales (8 per group), each rounded up to whole 64-lane loads
   const int ag = p.J << ls;                     // activation groups of the wave
   const int n_pieces = M * ag * kGroupPieces;
-  const int n_scales = M * ag * 8;
+  constexpr int MD = MF ? 4 : M;                // column slots of the scale array
+  const int n_scales = MD * ag * 8;
   const int act_rounds = (n_pieces + 63) >> 6;
   const int d_rounds = (n_scales + 63) >> 6;
   const int wave_dwords = JT * 1280 + act_rounds * 256 + d_rounds * 64;
   // what this workgroup actually loads and transposes (a short MoE group
   // stages only its own columns; the LDS carving above is for M)
   const int use_pieces = ncols * ag * kGroupPieces;
-  const int use_scales = ncols * ag * 8;
+  const int use_scales = (MF ? MD : ncols) * ag * 8;
   const int use_act_rounds = (use_pieces + 63) >> 6;
   const int use_d_rounds = (use_scales + 63) >> 6;
   uint32_t* wlds = lds + wave * wave_dwords;
@@ -574,11 +656,18 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
       const uint32_t m0d = lds_m0(dlds);
       for (int r = 0; r < use_d_rounds; ++r) {
         const int i = min(64 * r + lane, use_scales - 1);
-        const int g = i >> 3;
-        const int m = M == 1 ? 0 : ag_pow2 ? g >> ag_shift : g / ag;
-        const int lgl = g - m * ag;
-        dma4(p.d, (uint32_t)(4 * (token_of(m) * nb + group_of(lgl) * 8 + (i & 7))),
-             m0d + 256 * r);
+        if constexpr (MF) {
+          // [group][block][column slot]; slots past the last column re-read it
+          const int m = min(i & 3, ncols - 1);
+          dma4(p.d, (uint32_t)(4 * (token_of(m) * nb + group_of(i >> 5) * 8 + ((i >> 2) & 7))),
+               m0d + 256 * r);
+        } else {
+          const int g = i >> 3;
+          const int m = M == 1 ? 0 : ag_pow2 ? g >> ag_shift : g / ag;
+          const int lgl = g - m * ag;
+          dma4(p.d, (uint32_t)(4 * (token_of(m) * nb + group_of(lgl) * 8 + (i & 7))),
+               m0d + 256 * r);
+        }
       }
     }
 #pragma unroll
@@ -609,7 +698,9 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
     wait_chunks(min(JT, p.J - j) - 1);          // chunk j has landed
     __builtin_amdgcn_wave_barrier();
     uint32_t buf[20];
-    const uint4* src = reinterpret_cast<const uint4*>(wlds + buf_i * 1280 + 20 * lane);
+    // this lane's group: row slot `slot`, group t of the row's segment
+    const int gl = MF ? slot * L + t : lane;
+    const uint4* src = reinterpret_cast<const uint4*>(wlds + buf_i * 1280 + 20 * gl);
 #pragma unroll
     for (int k = 0; k < 5; ++k) {
       const uint4 v = src[k];
@@ -624,9 +715,13 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
       load_chunk(wb + (int64_t)((((j + JT) * p.wk) + wave) << ls) * 80, co,
                  ring_m0 + 5120 * buf_i);
     const int lgl = (j << ls) + t;
-    group_product<M, (M <= 4) && (!MOE || M == 1)>(buf, alds + lgl * kGroupDwords, act_stride,
-                                                  dlds + lgl * 8, ag * 8, acc, bad_lo, bad_hi,
-                                                  ncols);
+    if constexpr (MF)
+      group_product_mf<M>(buf, alds + min(lane & 3, ncols - 1) * act_stride + lgl * kGroupDwords,
+                          dlds + lgl * 32, acc, bad_lo, bad_hi);
+    else
+      group_product<M, (M <= 4) && (!MOE || M == 1)>(buf, alds + lgl * kGroupDwords, act_stride,
+                                                    dlds + lgl * 8, ag * 8, acc, bad_lo, bad_hi,
+                                                    ncols);
   }
 
   // row sum: xor shuffles over the L lanes of the row, then over the waves
@@ -634,7 +729,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     float v = bad ? __builtin_nanf("") : acc[m];
-    acc[m] = row_sum(v, L);
+    acc[m] = MF ? row_sum_mf(v, L) : row_sum(v, L);
   }
   const int S = 64 >> ls;
   if (p.wk > 1) {
@@ -668,13 +763,13 @@ using GemvFn = void (*)(Params);
 
 constexpr int kMaxChunksInFlight = 4;
 
-template <int M, bool MOE>
+template <int M, bool MOE, bool MF = false>
 GemvFn pick(int jt) {
   switch (jt) {
-    case 1: return gemv_kernel<M, 1, MOE, 0>;
-    case 2: return gemv_kernel<M, 2, MOE, 0>;
-    case 3: return gemv_kernel<M, 3, MOE, 0>;
-    default: return gemv_kernel<M, 4, MOE, 0>;
+    case 1: return gemv_kernel<M, 1, MOE, 0, MF>;
+    case 2: return gemv_kernel<M, 2, MOE, 0, MF>;
+    case 3: return gemv_kernel<M, 3, MOE, 0, MF>;
+    default: return gemv_kernel<M, 4, MOE, 0, MF>;
   }
 }
 

@@ -260,6 +260,19 @@ rfp2_status rfp2_debug_half_dots(const uint8_t* w, int64_t N, int64_t K,
   return from_hip(rfp2::launch_debug_half_dots(w, N, K, q, M, sums_out, stream));
 }
 
+rfp2_status rfp2_debug_half_sums_mf(const uint8_t* w, int64_t N, int64_t K,
+                                    const int8_t* q, int64_t M, int32_t* sums_out,
+                                    hipStream_t stream) {
+  if (!w || !q || !sums_out) return RFP2_E_NULL;
+  if (N < 1 || N > kMaxRows || M < 1 || M > kMaxRows || K < 256 || K % 256 != 0 ||
+      K > (int64_t(1) << 30))
+    return RFP2_E_SHAPE;
+  if (N * (K / 32) > (int64_t(1) << 40) / M) return RFP2_E_SHAPE;
+  if (!aligned(w, 2) || !aligned(q, 4) || !aligned(sums_out, 4)) return RFP2_E_ALIGN;
+  (void)hipGetLastError();
+  return from_hip(rfp2::launch_debug_half_sums_mf(w, N, K, q, M, sums_out, stream));
+}
+
 rfp2_status rfp2_debug_decode_f16(const uint8_t* w, int64_t N, int64_t K, int form,
                                   uint16_t* h_out, hipStream_t stream) {
   if (!w || !h_out) return RFP2_E_NULL;

@@ -338,6 +338,14 @@ rfp2_status rfp2_read_ceiling(const uint8_t* buf, int64_t bytes, uint32_t magic,
  * [M][N][K/32][2] int32.  Requires N >= 1, M >= 1, K >= 32, K % 32 == 0,
  * M * N * (K/32) <= 2^40; w 2-byte aligned, q 4-byte aligned.
  *
+ * rfp2_debug_half_sums_mf: the same int32 half sums as computed by the
+ * GEMV's matrix-core form of two to four columns (v_mfma_i32_4x4x4_16b_i8
+ * over quads of four rows at one 8-block group, one column's activations per
+ * lane; "03 · Runtime": the half's int8 products summed in int32 before any
+ * scale), sums_out [M][N][K/32][2] int32 as rfp2_debug_half_dots.  Requires
+ * N >= 1, M >= 1, K >= 256, K % 256 == 0, M * N * (K/32) <= 2^40; w 2-byte
+ * aligned, q 4-byte aligned.
+ *
  * rfp2_debug_decode_f16: the fp16 value (level x scale) each weight takes in
  * the fp16 matrix-core products, h_out [N][K] as IEEE half-precision bit
  * patterns in natural order (NaN for both halves of a block with an illegal
@@ -353,6 +361,9 @@ rfp2_status rfp2_debug_decode(const uint8_t* w, int64_t N, int64_t K,
 rfp2_status rfp2_debug_half_dots(const uint8_t* w, int64_t N, int64_t K,
                                  const int8_t* q, int64_t M,
                                  int32_t* sums_out, hipStream_t stream);
+rfp2_status rfp2_debug_half_sums_mf(const uint8_t* w, int64_t N, int64_t K,
+                                    const int8_t* q, int64_t M,
+                                    int32_t* sums_out, hipStream_t stream);
 rfp2_status rfp2_debug_decode_f16(const uint8_t* w, int64_t N, int64_t K, int form,
                                   uint16_t* h_out, hipStream_t stream);
 

@@ -64,6 +64,13 @@ def test_gemm_moe_quantize_argument_checks():
     assert L.rfp2_debug_half_dots(P, 1, 64, P, 0, P, None) == rf.RFP2_E_SHAPE
     # M * N * (K/32) beyond 2^40 half-sum pairs is refused before any launch
     assert L.rfp2_debug_half_dots(P, 1 << 20, 1 << 20, P, 1 << 20, P, None) == rf.RFP2_E_SHAPE
+    # the matrix-core half sums: whole 8-block groups per row only
+    assert L.rfp2_debug_half_sums_mf(P, 1, 64, P, 1, P, None) == rf.RFP2_E_SHAPE
+    assert L.rfp2_debug_half_sums_mf(P, 1, 288, P, 1, P, None) == rf.RFP2_E_SHAPE
+    assert L.rfp2_debug_half_sums_mf(P, 1, 256, P, 0, P, None) == rf.RFP2_E_SHAPE
+    assert L.rfp2_debug_half_sums_mf(P, 1 << 20, 1 << 20, P, 1 << 20, P, None) == rf.RFP2_E_SHAPE
+    assert L.rfp2_debug_half_sums_mf(P, 1, 256, P, 1, None, None) == rf.RFP2_E_NULL
+    assert L.rfp2_debug_half_sums_mf(P, 1, 256, P + 2, 1, P, None) == rf.RFP2_E_ALIGN
     assert L.rfp2_debug_decode_f16(P, 1, 64, 2, P, None) == rf.RFP2_E_SHAPE    # form 0 or 1
     assert L.rfp2_debug_decode_f16(P, 1, 48, 0, P, None) == rf.RFP2_E_SHAPE
     assert L.rfp2_debug_decode_f16(P, 1, 64, 1, None, None) == rf.RFP2_E_NULL

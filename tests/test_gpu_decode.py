@@ -134,6 +134,30 @@ def test_gemv_group_half_dots_all_bytes_both_parities(N, K, M):
     assert np.array_equal(got, oracle.half_sums(packed, N, K, q))
 
 
+@pytest.mark.parametrize("N,K,M", [(16, 1024, 4), (7, 256, 1), (9, 512, 3), (5, 2048, 6)])
+def test_gemv_mf_half_sums_all_bytes_both_parities(N, K, M):
+    # the int32 half sums of the GEMV's matrix-core form (4x4x4 int8 products
+    # over quads of four rows at one group), bit for bit: every code byte at
+    # even and odd block positions, extreme activations, ragged rows and
+    # column quads (M = 1, 3 and 6 leave column slots past the end)
+    announce("debug_half_sums_mf", N, K, M)
+    flat = parity_blocks(256)
+    packed = np.resize(flat, N * K // 32 * 10).reshape(N, K // 32 * 10)
+    q = synth.uniform_bytes(M * K, 0, 254, seed=29 + M).view(np.int8).reshape(M, K)
+    q = np.where(q == -128, -127, q).astype(np.int8)
+    q[0, :64] = 127
+    q[-1, 64:128] = -127
+    ref = oracle.half_sums(packed, N, K, q)
+    sums = empty((M, N, K // 32, 2), torch.int32)
+    rf.rfp2_debug_half_sums_mf(to_dev(packed.reshape(-1)), N, K, to_dev(q), M, sums)
+    assert np.array_equal(host(sums).astype(np.int64), ref)
+    if M == 1 and N == 7:
+        # the dot4 form of the same sums agrees as well
+        dots = empty((M, N, K // 32, 2), torch.int32)
+        rf.rfp2_debug_half_dots(to_dev(packed.reshape(-1)), N, K, to_dev(q), M, dots)
+        assert np.array_equal(host(dots), host(sums))
+
+
 @pytest.mark.parametrize("form", [0, 1])
 @pytest.mark.parametrize("N,K", [(16, 1024), (3, 96), (5, 32)])
 def test_f16_decode_bitexact(form, N, K):

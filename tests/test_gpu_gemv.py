@@ -38,11 +38,15 @@ def test_gemv_512x2048_full_oracle_weights():
 
 # (N, K, M): ragged row counts, every lanes-per-row geometry (K/256 = 1, 3, 5,
 # 8, 10, 16, 20, 28, 56, 64, 128 groups), 1..8 columns and column chunking (the
-# largest K with eight columns runs as eight one-column launches).
+# largest K with eight columns runs as eight one-column launches).  Two to
+# four columns run the matrix-core form at 1, 2, 4, 8 and 16 lanes per row
+# (257x768, 200x5120, 130x4096, 70x14336, 33x16384) and fall back to the dot
+# form at 32 (45x32768 with two columns).
 SHAPES = [
     (1, 256, 1), (300, 256, 1), (257, 768, 3), (1000, 1280, 2), (123, 2560, 5),
     (96, 4096, 8), (200, 5120, 4), (130, 7168, 7), (64, 16384, 1), (37, 32768, 1),
     (70, 16384, 8), (513, 2048, 6), (45, 32768, 8), (50, 14336, 1),
+    (130, 4096, 2), (70, 14336, 4), (33, 16384, 3), (45, 32768, 2), (5, 256, 4),
 ]
 
 
