@@ -178,12 +178,6 @@ __global__ __launch_bounds__(256) void debug_half_sums_mf_kernel(
   }
 }
 
-// k order of expand_half_f16's 16 fp16 values (position e holds weight
-// kOrder[e] of the half).
-__device__ __forceinline__ int f16_weight_of(int e) {
-  return (e & 8) + ((e >> 1) & 3) + 4 * (e & 1);
-}
-
 // fp16 bits of the 16 weights of one half, in natural order, from 8 dwords
 // in the k order of expand_half_f16.
 __device__ __forceinline__ void store_half_f16(const uint32_t (&o)[8], uint16_t* out) {
@@ -194,7 +188,6 @@ __device__ __forceinline__ void store_half_f16(const uint32_t (&o)[8], uint16_t*
 
 __global__ __launch_bounds__(256) void debug_decode_f16_kernel(
     const uint8_t* __restrict__ w, int64_t nblocks, int form, uint16_t* __restrict__ out) {
-  const float fix = scale_fix();
   const int64_t npairs = (nblocks + 1) / 2;
   for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < npairs;
        p += (int64_t)gridDim.x * 256) {
@@ -204,7 +197,7 @@ __global__ __launch_bounds__(256) void debug_decode_f16_kernel(
     if (form == 0) {
       for (int blk = 0; blk < nblk; ++blk) {
         uint32_t h0[8], h1[8];
-        decode_pair_block_f16(wd, blk, fix, h0, h1);
+        decode_pair_block_f16(wd, blk, h0, h1);
         store_half_f16(h0, out + (2 * p + blk) * 32);
         store_half_f16(h1, out + (2 * p + blk) * 32 + 16);
       }
@@ -213,13 +206,13 @@ __global__ __launch_bounds__(256) void debug_decode_f16_kernel(
       for (int kh = 0; kh < 2; ++kh) {
         v8h a0, a1;
         uint32_t o[8];
-        decode_half<0>(wp, kh, fix, a0, a1);
+        decode_half<0>(wp, kh, a0, a1);
         const uint4 x0 = __builtin_bit_cast(uint4, a0), x1 = __builtin_bit_cast(uint4, a1);
         o[0] = x0.x; o[1] = x0.y; o[2] = x0.z; o[3] = x0.w;
         o[4] = x1.x; o[5] = x1.y; o[6] = x1.z; o[7] = x1.w;
         store_half_f16(o, out + (2 * p) * 32 + 16 * kh);
         if (nblk == 2) {
-          decode_half<1>(wp, kh, fix, a0, a1);
+          decode_half<1>(wp, kh, a0, a1);
           const uint4 y0 = __builtin_bit_cast(uint4, a0), y1 = __builtin_bit_cast(uint4, a1);
           o[0] = y0.x; o[1] = y0.y; o[2] = y0.z; o[3] = y0.w;
           o[4] = y1.x; o[5] = y1.y; o[6] = y1.z; o[7] = y1.w;

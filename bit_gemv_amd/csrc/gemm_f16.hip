@@ -26,10 +26,11 @@
 // (as gemm.hip).  The routed form (tokens sorted by expert, a prompt batch
 // through the routed experts) has a kernel of its own below
 // (moe_gemm_kernel): 64-token tiles, each inside one expert's slots, with
-// the weights decoded straight into registers.  Within each 16-weight half the k order in LDS is
-// 0,4, 1,5, 2,6, 3,7, 8,12, 9,13, 10,14, 11,15 for weights and activations
-// alike (the order the decode produces cheaply); a dot product over the half
-// does not depend on it.
+// the weights decoded straight into registers.  Within each 16-weight half
+// the k order in LDS is 0,8, 4,12, 1,9, 5,13, 2,10, 6,14, 3,11, 7,15 for
+// weights and activations alike (the order in which one byte permute per
+// pair of weights decodes them); a dot product over the half does not
+// depend on it.
 #include "f16_decode.h"
 #include "rfp2_internal.h"
 
@@ -89,10 +90,10 @@ __device__ __forceinline__ void fetch(PrefetchF16& f, const RowPtrs& r, int kb, 
 
 template <int TM>
 __device__ __forceinline__ void stage_to_lds(const PrefetchF16& f, StageF16<TM>& st, int tid,
-                                             float fix, bool acts) {
+                                             bool acts) {
   const int wrow = tid >> 1, blk = tid & 1;
   uint32_t h0[8], h1[8];
-  decode_pair_block_f16(f.wd, blk, fix, h0, h1);
+  decode_pair_block_f16(f.wd, blk, h0, h1);
   uint4* dst = reinterpret_cast<uint4*>(st.wh + wrow * kRowBytes + blk * 64);
   dst[0] = make_uint4(h0[0], h0[1], h0[2], h0[3]);
   dst[1] = make_uint4(h0[4], h0[5], h0[6], h0[7]);
@@ -204,7 +205,6 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_kernel(GemmF16Params p) {
   const int64_t row_bytes = (int64_t)(K / 32) * 10;
   const int nb = K / 32;
   const int stages = nb / BKB;
-  const float fix = scale_fix();
 
   // tile -> (tokens, rows): XCD-aware order over (m, n) tiles as in gemm.hip
   int tile = blockIdx.x;
@@ -241,12 +241,12 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_kernel(GemmF16Params p) {
   // so the matrix-core and vector work of an iteration can be interleaved.
   PrefetchF16 f;
   fetch(f, rp, 0, tid, acts);
-  stage_to_lds(f, sm[0], tid, fix, acts);
+  stage_to_lds(f, sm[0], tid, acts);
   fetch(f, rp, stages > 1 ? BKB : 0, tid, acts);
   __syncthreads();
   for (int s = 0; s + 1 < stages; ++s) {
     compute_stage(sm[s & 1], lane, wm, wn, acc);
-    stage_to_lds(f, sm[(s + 1) & 1], tid, fix, acts);
+    stage_to_lds(f, sm[(s + 1) & 1], tid, acts);
     const int next = s + 2 < stages ? s + 2 : stages - 1;
     fetch(f, rp, next * BKB, tid, acts);
     __syncthreads();
@@ -376,7 +376,6 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_kernel(GemmF16Params p) {
   const int64_t row_bytes = (int64_t)(K / 32) * 10;
   const int nb = K / 32;
   const int nst = nb / kMoeKB;                  // K % 256 == 0
-  const float fix = scale_fix();
 
   // token tile i runs on XCD i % 8 with all of its row tiles (its gathered
   // activations stay in that XCD's L2); workgroups past the last tile leave
@@ -416,24 +415,24 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_kernel(GemmF16Params p) {
     load_acts(ap, qrow, drow, kb_next);
     __syncthreads();
     v8h a0, a1;
-    decode_half<0>(w0, kh, fix, a0, a1);
+    decode_half<0>(w0, kh, a0, a1);
     moe_block(sm, 0, lane, a0, a1, two, acc);
-    decode_half<1>(w0, kh, fix, a0, a1);
+    decode_half<1>(w0, kh, a0, a1);
     load_pair(w0, wrow, kb_next + 0);
     moe_block(sm, 1, lane, a0, a1, two, acc);
-    decode_half<0>(w1, kh, fix, a0, a1);
+    decode_half<0>(w1, kh, a0, a1);
     moe_block(sm, 2, lane, a0, a1, two, acc);
-    decode_half<1>(w1, kh, fix, a0, a1);
+    decode_half<1>(w1, kh, a0, a1);
     load_pair(w1, wrow, kb_next + 2);
     moe_block(sm, 3, lane, a0, a1, two, acc);
-    decode_half<0>(w2, kh, fix, a0, a1);
+    decode_half<0>(w2, kh, a0, a1);
     moe_block(sm, 4, lane, a0, a1, two, acc);
-    decode_half<1>(w2, kh, fix, a0, a1);
+    decode_half<1>(w2, kh, a0, a1);
     load_pair(w2, wrow, kb_next + 4);
     moe_block(sm, 5, lane, a0, a1, two, acc);
-    decode_half<0>(w3, kh, fix, a0, a1);
+    decode_half<0>(w3, kh, a0, a1);
     moe_block(sm, 6, lane, a0, a1, two, acc);
-    decode_half<1>(w3, kh, fix, a0, a1);
+    decode_half<1>(w3, kh, a0, a1);
     load_pair(w3, wrow, kb_next + 6);
     moe_block(sm, 7, lane, a0, a1, two, acc);
   }
