@@ -21,10 +21,17 @@
 //     same within-half permutation (transpose_half), so the dot product over
 //     each half is unchanged.  Row strides of 136 bytes keep the 8-byte LDS
 //     operand reads of 32 lanes on distinct banks.
-//   * The fp32 rescale of every (token, row, block) is vector-ALU work (two
-//     int->fp32 converts and three multiply-adds) that no MFMA shape removes:
-//     per-half weight scales and per-block activation scales both vary along
-//     K.  It, not the matrix cores, bounds this kernel.
+//   * The fp32 rescale of every (token, row, block) is vector-ALU work that
+//     no MFMA shape removes: per-half weight scales and per-block activation
+//     scales both vary along K.  It, not the matrix cores, bounds this
+//     kernel.  Four instructions instead of five: the first half's partial
+//     is accumulated onto the int32 bit pattern of 1.5 * 2^23, so the result
+//     read as fp32 is exactly 1.5 * 2^23 + P0 (|P0| <= 16 * 4 * 127 < 2^22),
+//     and s0 * P0 = fma(s0, that, -1.5 * 2^23 * s0) in one instruction,
+//     exact (s0 has at most 4 significant bits, s0 * P0 at most 17) -- the
+//     same value as the convert and multiply it replaces, so the outputs
+//     are unchanged; then one convert of P1, fma(s1, P1, s0 * P0), and the
+//     fma with the activation scale.
 //   * Workgroup -> tile order is XCD-aware: the hardware deals workgroups to
 //     the 8 XCDs round-robin, so consecutive tiles are given to workgroups
 //     that land on the same XCD, and the token tiles of one row tile run
@@ -152,6 +159,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) facc[i][j][r] = 0.0f;
 
+  // the accumulator start of the first half's partials: fp32 1.5 * 2^23
+  v16i kBias;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) kBias[r] = 0x4B400000;
   Prefetch f;
   fetch(f, w, q, d, row_bytes, K, nb, 0, tid, n0, m0, N, M);
   const int koff_lane = 8 * (lane >> 5);
@@ -178,9 +189,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(
         const long b1 =
             *reinterpret_cast<const long*>(st.wq + n * kStride + blk * 32 + 16 + koff_lane);
         const float2 sc = *reinterpret_cast<const float2*>(&st.ws[n][2 * blk]);
+        const float nb0 = -12582912.0f * sc.x;
 #pragma unroll
         for (int tm = 0; tm < 2; ++tm) {
-          const v16i P0 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a[0][tm], b0, v16i{}, 0, 0, 0);
+          const v16i P0 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a[0][tm], b0, kBias, 0, 0, 0);
           const v16i P1 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a[1][tm], b1, v16i{}, 0, 0, 0);
           // lane holds row n of the tile and tokens
           // (r % 4) + 8 * (r / 4) + 4 * (lane / 32), r = 0..15
@@ -192,7 +204,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * p + e;
-              const float t = fmaf(sc.y, (float)P1[r], sc.x * (float)P0[r]);
+              const float t = fmaf(sc.y, (float)P1[r], fmaf(sc.x, __int_as_float(P0[r]), nb0));
               facc[tm][tn][r] = fmaf(dd[e], t, facc[tm][tn][r]);
             }
           }
