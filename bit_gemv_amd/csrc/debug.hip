@@ -162,7 +162,12 @@ __global__ __launch_bounds__(256) void debug_half_sums_mf_kernel(
       uint32_t T0[4], T1[4];
       transpose_half(X0, T0);
       transpose_half(X1, T1);
-      const v4i S0 = half_sums_mf(W0, make_uint4(T0[0], T0[1], T0[2], T0[3]));
+      // half 0 from the product's biased start (the int32 pattern of fp32
+      // 1.5 * 2^23), the bias taken off again in integer arithmetic
+      constexpr int kBias = 0x4B400000;
+      const v4i S0 = half_sums_mf(W0, make_uint4(T0[0], T0[1], T0[2], T0[3]),
+                                  v4i{kBias, kBias, kBias, kBias}) -
+                     v4i{kBias, kBias, kBias, kBias};
       const v4i S1 = half_sums_mf(W1, make_uint4(T1[0], T1[1], T1[2], T1[3]));
       if (store && n < N) {
 #pragma unroll

@@ -176,8 +176,10 @@ __device__ __forceinline__ void group_product(const uint32_t (&dw)[20],
 // four columns per block.  Column slots past M (M < 4) compute unused sums.
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ v4i half_sums_mf(const uint32_t (&W)[4], const uint4& A) {
-  v4i s = __builtin_amdgcn_mfma_i32_4x4x4i8((int)A.x, (int)W[0], v4i{0, 0, 0, 0}, 0, 0, 0);
+// `start` is the accumulator's initial value (zero, or the bias below).
+__device__ __forceinline__ v4i half_sums_mf(const uint32_t (&W)[4], const uint4& A,
+                                            v4i start = v4i{0, 0, 0, 0}) {
+  v4i s = __builtin_amdgcn_mfma_i32_4x4x4i8((int)A.x, (int)W[0], start, 0, 0, 0);
   s = __builtin_amdgcn_mfma_i32_4x4x4i8((int)A.y, (int)W[1], s, 0, 0, 0);
   s = __builtin_amdgcn_mfma_i32_4x4x4i8((int)A.z, (int)W[2], s, 0, 0, 0);
   s = __builtin_amdgcn_mfma_i32_4x4x4i8((int)A.w, (int)W[3], s, 0, 0, 0);
@@ -210,12 +212,18 @@ __device__ __forceinline__ void group_product_mf(const uint32_t (&dw)[20], const
       bad_lo |= sc;
     else
       bad_hi |= sc;
-    const v4i S0 = half_sums_mf(W0, A0);
+    // half 0's sums start from the int32 bit pattern of fp32 1.5 * 2^23, so
+    // read as fp32 they are exactly 1.5 * 2^23 + S0 (|S0| <= 16 * 4 * 127 <
+    // 2^22) and s0 * S0 = fma(s0, that, -1.5 * 2^23 * s0) is one exact
+    // instruction (s0 has at most 4 significant bits, s0 * S0 at most 17):
+    // the value the convert and the multiply give, one instruction fewer
+    const v4i S0 = half_sums_mf(W0, A0, v4i{0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000});
     const v4i S1 = half_sums_mf(W1, A1);
+    const float nb0 = -12582912.0f * s0;
     const float dm[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
     for (int m = 0; m < M; ++m)
-      acc[m] = fmaf(dm[m], fmaf(s1, (float)S1[m], s0 * (float)S0[m]), acc[m]);
+      acc[m] = fmaf(dm[m], fmaf(s1, (float)S1[m], fmaf(s0, __int_as_float(S0[m]), nb0)), acc[m]);
   }
 }
 
