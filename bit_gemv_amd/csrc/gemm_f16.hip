@@ -16,7 +16,8 @@
 //     core's fp32 accumulation may round, each step within 2^-24 of the
 //     running sum;
 //   * the epilogue per (token, row, block) is one FMA, y += d * C, against
-//     two int->fp32 converts and three FMAs for the int32 per-half partials.
+//     four instructions for the int32 per-half partials (a convert and three
+//     FMAs, the first half's convert folded into a biased accumulator).
 // The rescale, not the matrix cores, bounds the int8 path; here the two are
 // of the same order.
 //
