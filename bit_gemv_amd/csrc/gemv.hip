@@ -163,13 +163,16 @@ Geometry geometry(int64_t K, int64_t M, int64_t rows_total) {
 // Per wave: jt chunk buffers, the activations (kGroupPieces 16-byte pieces
 // per column and group) and their scales (four column slots per block in the
 // matrix-core form), each rounded up to whole 64-lane loads; then the
-// cross-wave partial sums.  Must match the carving in gemv_kernel.
-size_t lds_bytes(int M, const Geometry& g, bool mf = false) {
+// cross-wave partial sums.  The routed matrix-core form (exact) carves the
+// activations exactly and keeps the partial sums in the chunk buffers.  Must
+// match the carving in gemv_kernel.
+size_t lds_bytes(int M, const Geometry& g, bool mf = false, bool exact = false) {
   const size_t ag = (size_t)g.J << g.lshift;
   const size_t act_rounds = (M * ag * kGroupPieces + 63) / 64;
+  const size_t act_dwords = exact ? M * ag * kGroupPieces * 4 : act_rounds * 256;
   const size_t d_rounds = ((mf ? 4 : M) * ag * 8 + 63) / 64;
-  const size_t per_wave = (size_t)g.jt * 1280 + act_rounds * 256 + d_rounds * 64;
-  return (g.wk * per_wave + (size_t)g.wk * g.rows * M) * 4;
+  const size_t per_wave = (size_t)g.jt * 1280 + act_dwords + d_rounds * 64;
+  return (g.wk * per_wave + (exact ? 0 : (size_t)g.wk * g.rows * M)) * 4;
 }
 
 int compute_units() {
@@ -250,7 +253,8 @@ namespace {
 Geometry tokens_geometry(int64_t K, int T) {
   for (int j = std::max(2, T / 2);; --j) {
     const Geometry g = pick_geometry(K, j);
-    if (j == 1 || lds_bytes(T, g, use_mf(T, g.lshift)) <= (size_t)kMaxLdsBytesPerBlock)
+    const bool mf = use_mf(T, g.lshift);
+    if (j == 1 || lds_bytes(T, g, mf, mf) <= (size_t)kMaxLdsBytesPerBlock)
       return g;
   }
 }
@@ -262,7 +266,9 @@ hipError_t launch_moe_gemv_tokens(const uint8_t* w, int64_t E, int64_t N, int64_
                                   hipStream_t stream) {
   int cols = (int)T;
   Geometry g = tokens_geometry(K, cols);
-  while (cols > 1 && lds_bytes(cols, g, use_mf(cols, g.lshift)) > (size_t)kMaxLdsBytesPerBlock)
+  while (cols > 1 &&
+         lds_bytes(cols, g, use_mf(cols, g.lshift), use_mf(cols, g.lshift)) >
+             (size_t)kMaxLdsBytesPerBlock)
     g = tokens_geometry(K, --cols);
   const int64_t nb = K / 32;
   for (int64_t t0 = 0; t0 < T; t0 += cols) {
@@ -279,7 +285,7 @@ hipError_t launch_moe_gemv_tokens(const uint8_t* w, int64_t E, int64_t N, int64_
                ids_c, (int)E, err, (int)top_k, (int)(tc * top_k), nullptr, nullptr, nullptr};
       const bool mf = use_mf(tc, gc.lshift);
       hipLaunchKernelGGL(gemv_detail::pick_moe_tokens(tc, mf), grid, dim3(64 * gc.wk),
-                         lds_bytes(tc, gc, mf), stream, p);
+                         lds_bytes(tc, gc, mf, mf), stream, p);
       e = hipGetLastError();
     }
     if (e != hipSuccess) return e;

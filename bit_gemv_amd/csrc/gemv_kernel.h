@@ -560,7 +560,16 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
   const int n_scales = MD * ag * 8;
   const int act_rounds = (n_pieces + 63) >> 6;
   const int d_rounds = (n_scales + 63) >> 6;
-  const int wave_dwords = JT * 1280 + act_rounds * 256 + d_rounds * 64;
+  // The routed matrix-core form carves the activations exactly (the last
+  // load round only partly used) and keeps the cross-wave partial sums in the
+  // chunk ring, which takes a four-token workgroup (4 waves, 4 groups each)
+  // from 45 KB to 39 KB: four per compute unit instead of three (128 experts
+  // of 1536 x 4096, top-8, four tokens: 13.05 -> 12.27 us with half of the
+  // experts shared, 18.82 -> 17.08 us with none; the dense form, whose
+  // workgroups all fit anyway, lost 2 % with it).
+  constexpr bool EXACT = MF && MOE;
+  const int act_dwords = EXACT ? n_pieces * 4 : act_rounds * 256;
+  const int wave_dwords = JT * 1280 + act_dwords + d_rounds * 64;
   // what this workgroup actually loads and transposes (a short MoE group
   // stages only its own columns; the LDS carving above is for M)
   const int use_pieces = ncols * ag * kGroupPieces;
@@ -569,7 +578,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
   const int use_d_rounds = (use_scales + 63) >> 6;
   uint32_t* wlds = lds + wave * wave_dwords;
   uint32_t* alds = wlds + JT * 1280;
-  float* dlds = reinterpret_cast<float*>(alds + act_rounds * 256);
+  float* dlds = reinterpret_cast<float*>(alds + act_dwords);
   const int nb = K >> 5;
   auto group_of = [&](int lgl) {
     return (((lgl >> ls) * p.wk + wave) << ls) + (lgl & (L - 1));
@@ -659,7 +668,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
         const int tok = token_of(m);
         const uint32_t off =
             used ? (uint32_t)(tok * K + (group_of(lgl) * 16 + piece) * 16) : 0u;
-        dma16(p.q, off, m0 + 1024 * r);
+        if (!EXACT || pc < n_pieces) dma16(p.q, off, m0 + 1024 * r);
       }
       const uint32_t m0d = lds_m0(dlds);
       for (int r = 0; r < use_d_rounds; ++r) {
@@ -741,17 +750,20 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
   }
   const int S = 64 >> ls;
   if (p.wk > 1) {
-    float* red = reinterpret_cast<float*>(lds + p.wk * wave_dwords);
+    // wave wv's sums at red + wv * red_stride (EXACT: the start of the
+    // wave's own chunk ring, free once its last chunk is read)
+    float* red = reinterpret_cast<float*>(EXACT ? lds : lds + p.wk * wave_dwords);
+    const int red_stride = EXACT ? wave_dwords : S * M;
     if (t == 0) {
 #pragma unroll
-      for (int m = 0; m < M; ++m) red[(wave * S + slot) * M + m] = acc[m];
+      for (int m = 0; m < M; ++m) red[wave * red_stride + slot * M + m] = acc[m];
     }
     __syncthreads();
     if (wave == 0 && t == 0) {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         float v = red[slot * M + m];
-        for (int wv = 1; wv < p.wk; ++wv) v += red[(wv * S + slot) * M + m];
+        for (int wv = 1; wv < p.wk; ++wv) v += red[wv * red_stride + slot * M + m];
         acc[m] = v;
       }
     }
