@@ -123,9 +123,18 @@ struct Geometry {
 //     current one is in registers, and a deeper ring costs more LDS than it
 //     hides latency.
 constexpr int64_t kMinWorkgroupsForJ2 = 512;
+// wave slots of a compute unit the matrix-core GEMV's workgroups can use
+// (86 registers: five waves per SIMD)
+constexpr int64_t kWaveSlotsPerCu = 20;
 
-// max_ag: the most groups a wave may cover (J * L), for forms that need it
-Geometry pick_geometry(int64_t K, int j_target, int max_ag = 1 << 30) {
+struct AnySplit {
+  bool operator()(const Geometry&) const { return true; }
+};
+
+// max_ag: the most groups a wave may cover (J * L), for forms that need it;
+// ok: a further condition on the split
+template <typename Ok = AnySplit>
+Geometry pick_geometry(int64_t K, int j_target, int max_ag = 1 << 30, Ok ok = Ok{}) {
   static constexpr int kWaveRank[kMaxWaves + 1] = {99, 7, 4, 2, 0, 1, 3, 6, 5};
   const int G = (int)(K / 256);
   Geometry best{};
@@ -137,6 +146,7 @@ Geometry pick_geometry(int64_t K, int j_target, int max_ag = 1 << 30) {
       if ((G / L) % wk) continue;
       const int J = G / L / wk;
       if ((J << ls) > max_ag) continue;
+      if (!ok(Geometry{ls, wk, J, 1, 64 >> ls})) continue;
       // smaller is better: distance from the target J (ties: fewer groups),
       // then the wave-count rank, then fewer lanes per row (more rows)
       const int64_t key = ((int64_t)std::abs(J - j_target) << 32) |
@@ -175,6 +185,46 @@ size_t lds_bytes(int M, const Geometry& g, bool mf = false, bool exact = false) 
   return (g.wk * per_wave + (exact ? 0 : (size_t)g.wk * g.rows * M)) * 4;
 }
 
+int compute_units();
+
+// Two to four dense columns (the matrix-core form): the one-column rule's
+// split as long as all of its workgroups fit on the chip at once (LDS over
+// the workgroups a compute unit holds), else the first of these that does:
+// one lane per row and four waves (64 rows per workgroup) if that gives
+// every compute unit a workgroup, one group per lane, the split with J
+// nearest 2.  A launch that needs two rounds of workgroups loses 7-60 %
+// (alternating same-box timings, M = 4: 32768 x 4096 14.57 -> 13.58 us,
+// 14336 x 4096 10.10 -> 8.44, 18432 x 7168 27.92 -> 17.64, 4096 x 14336
+// 23.43 -> 9.64).  Where the usual split fits, it stays: one lane per row
+// instead was 8 % slower at 16384 x 4096 and within 2 % at 16384 x 5120
+// and 28672 x 4096.
+Geometry columns_geometry(int64_t K, int M, int64_t rows_total) {
+  const int64_t cus = compute_units();
+  auto one_round = [&](const Geometry& g) {
+    const size_t lds = lds_bytes(M, g, use_mf(M, g.lshift));
+    const int64_t per_cu = std::max<int64_t>(
+        1, std::min<int64_t>((int64_t)kMaxLdsBytesPerBlock / (int64_t)lds, kWaveSlotsPerCu / g.wk));
+    return (rows_total + g.rows - 1) / g.rows <= cus * per_cu;
+  };
+  auto workgroups = [&](const Geometry& g) { return (rows_total + g.rows - 1) / g.rows; };
+  const Geometry g2 = pick_geometry(K, 2);
+  if (workgroups(g2) >= kMinWorkgroupsForJ2) {
+    if (one_round(g2)) return g2;
+  } else {
+    const Geometry g1 = pick_geometry(K, 1);
+    if (one_round(g1)) return g1;
+  }
+  const int G = (int)(K / 256);
+  if (G % 4 == 0) {
+    const Geometry g{0, 4, G / 4, 1, 64};
+    if (workgroups(g) >= cus && one_round(g)) return g;
+  }
+  const Geometry g1 = pick_geometry(K, 1);
+  if (one_round(g1)) return g1;
+  const Geometry g = pick_geometry(K, 2, 1 << 30, one_round);
+  return g.wk > 0 ? g : g1;
+}
+
 int compute_units() {
   static std::atomic<int> cached[64];
   int dev = 0;
@@ -202,7 +252,7 @@ int compute_units() {
 // as fit 64 KiB.
 hipError_t launch_gemv(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
                        const float* d, int64_t M, float* y, hipStream_t stream) {
-  const Geometry g = geometry(K, M, N);
+  const Geometry g = M >= 2 && M <= 4 ? columns_geometry(K, (int)M, N) : geometry(K, M, N);
   const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows));
   const int64_t cus = compute_units();
   const int64_t share = ((int64_t)grid.x + cus - 1) / cus;

@@ -120,6 +120,25 @@ def test_gemv_full_size_sampled_rows(name):
     assert np.isfinite(y).all()
 
 
+# Large matrices whose usual split of K would need two rounds of workgroups,
+# so the launch takes another: one lane per row over 64-row workgroups
+# (32768 x 4096, 18432 x 7168: seven groups per lane) or the one-round split
+# nearest two groups per lane (4096 x 14336: 16 lanes per row, seven waves;
+# 14336 x 4096 with two and three columns).
+@pytest.mark.parametrize("N,K,M", [(32768, 4096, 4), (18432, 7168, 4), (4096, 14336, 4),
+                                   (14336, 4096, 3), (14336, 4096, 2)])
+def test_gemv_one_round_splits(N, K, M):
+    announce("gemv one-round split", N, K, M)
+    packed = random_blocks(N, K, seed=N + M, scale_lo=0x00, scale_hi=0x30)
+    q, d = oracle.quantize_acts(synth.activations(M, K, seed=60 + M))
+    y = run_gemv(packed, N, K, q, d)
+    rows = sample_rows(N, 48, seed=N)
+    assert_within_bound(y[:, rows], oracle.ref_gemv(packed[rows], len(rows), K, q, d),
+                        oracle.abs_product_sums(packed[rows], len(rows), K, q, d),
+                        f"gemv {N}x{K} M={M}")
+    assert np.isfinite(y).all()
+
+
 @pytest.mark.parametrize("M", [6, 7, 8])
 def test_gemv_many_columns_large_matrix(M):
     # 16384 x 5120 with 6 and 7 columns runs as one launch whose workgroups
