@@ -76,13 +76,15 @@ def test_gemv_columns_are_independent():
                             f"column {m} alone vs in a batch of 4")
 
 
-def test_gemv_illegal_scale_gives_nan_row():
-    announce("gemv illegal scale byte")
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_gemv_illegal_scale_gives_nan_row(M):
+    # one column: the dot4 form; two to four: the matrix-core form
+    announce("gemv illegal scale byte", M)
     N, K = 64, 1024
     packed = random_blocks(N, K, seed=2, scale_hi=0x20)
     packed[5, 10 * 7 + 9] = 0x7F           # e1 of block 7 of row 5
     packed[9, 10 * 30 + 8] = 0x91          # e0 of block 30 of row 9
-    q, d = oracle.quantize_acts(synth.activations(2, K))
+    q, d = oracle.quantize_acts(synth.activations(M, K))
     y = run_gemv(packed, N, K, q, d)
     assert np.isnan(y[:, 5]).all() and np.isnan(y[:, 9]).all()
     ok = np.ones(N, bool)
