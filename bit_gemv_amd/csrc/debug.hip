@@ -14,7 +14,7 @@
 //     by block_half_sums against activations transposed as the GEMV stages
 //     them.
 //   * GEMV matrix-core half sums (rfp2_debug_half_sums_mf): the same blocks
-//     summed by half_sums_mf, the 4x4x4 int8 matrix-core form of two to four
+//     summed by half_sums_mf, the 4x4x4 int8 matrix-core form of two to eight
 //     columns, with its lane layout: quads of lanes are four rows at one
 //     group, each lane supplies one column's activations.
 //   * fp16 decode (rfp2_debug_decode_f16): pairs of blocks, as the fp16

@@ -38,18 +38,17 @@
 //     (see expand_half), and one pad piece so that the lanes of a row, which
 //     read neighbouring groups, hit different banks.  The per-block scales
 //     sit in an array of their own.
-//   * Two to four columns (dense, or a routed group of up to four tokens)
+//   * Two to eight columns (dense, or a routed group of several tokens)
 //     take the int32 half sums from the matrix cores instead of dot4 chains:
 //     v_mfma_i32_4x4x4_16b_i8 is sixteen 4x4x4 products, one per quad of
 //     lanes, so a quad holds four rows at the same group (their expanded
 //     weight words as B) and one column's activations per lane (as A), and
-//     each lane receives its row's half sums for all four columns.  The
-//     integers are those of the dot4 chains and the scale arithmetic is
-//     unchanged, so the outputs are bit for bit the same; the vector work
-//     per block and column drops from 13 instructions to 5 (16384 x 5120:
-//     M = 2, 3, 4 from 10.1, 12.9, 14.0 us to 9.6, 10.2, 11.6 us; 128
-//     experts of 1536 x 4096, top-8, four tokens sharing half their experts
-//     with the token before: 13.6 to 13.2 us).
+//     each lane receives its row's half sums for four columns (a second set
+//     of products for columns 4..7).  The integers are those of the dot4
+//     chains, so the outputs are those of the dot4 form; the vector work per
+//     block and column drops from 13 instructions to about 4 (16384 x 5120:
+//     M = 2, 3, 4 from 10.1, 12.9, 14.0 us to 9.6, 10.2, 11.6 us; M = 8 from
+//     25.3 us in two launches to 15.4 us in one).
 
 #include "gemv_kernel.h"
 
@@ -71,6 +70,10 @@ GemvFn pick_m8(int jt);
 GemvFn pick_m2_mf(int jt);
 GemvFn pick_m3_mf(int jt);
 GemvFn pick_m4_mf(int jt);
+GemvFn pick_m5_mf(int jt);
+GemvFn pick_m6_mf(int jt);
+GemvFn pick_m7_mf(int jt);
+GemvFn pick_m8_mf(int jt);
 }  // namespace gemv_detail
 
 namespace {
@@ -90,15 +93,19 @@ GemvFn pick_kernel(int M, int jt) {
   }
 }
 
-// The matrix-core form (two to four dense columns; a quad of lanes is four
-// rows at one group, so at most 16 lanes per row).
-bool use_mf(int M, int lshift) { return M >= 2 && M <= 4 && lshift <= 4; }
+// The matrix-core form (two to eight columns; a quad of lanes is four rows
+// at one group, so at most 16 lanes per row).
+bool use_mf(int M, int lshift) { return M >= 2 && M <= 8 && lshift <= 4; }
 
 GemvFn pick_mf(int M, int jt) {
   switch (M) {
     case 2: return pick_m2_mf(jt);
     case 3: return pick_m3_mf(jt);
-    default: return pick_m4_mf(jt);
+    case 4: return pick_m4_mf(jt);
+    case 5: return pick_m5_mf(jt);
+    case 6: return pick_m6_mf(jt);
+    case 7: return pick_m7_mf(jt);
+    default: return pick_m8_mf(jt);
   }
 }
 
@@ -123,9 +130,9 @@ struct Geometry {
 //     current one is in registers, and a deeper ring costs more LDS than it
 //     hides latency.
 constexpr int64_t kMinWorkgroupsForJ2 = 512;
-// wave slots of a compute unit the matrix-core GEMV's workgroups can use
-// (86 registers: five waves per SIMD)
-constexpr int64_t kWaveSlotsPerCu = 20;
+// wave slots of a compute unit the matrix-core GEMV's workgroups can use:
+// five waves per SIMD up to four columns (86 registers), four beyond
+int64_t wave_slots_per_cu(int M) { return M <= 4 ? 20 : 16; }
 
 struct AnySplit {
   bool operator()(const Geometry&) const { return true; }
@@ -180,7 +187,7 @@ size_t lds_bytes(int M, const Geometry& g, bool mf = false, bool exact = false) 
   const size_t ag = (size_t)g.J << g.lshift;
   const size_t act_rounds = (M * ag * kGroupPieces + 63) / 64;
   const size_t act_dwords = exact ? M * ag * kGroupPieces * 4 : act_rounds * 256;
-  const size_t d_rounds = ((mf ? 4 : M) * ag * 8 + 63) / 64;
+  const size_t d_rounds = ((mf ? 4 * ((M + 3) / 4) : M) * ag * 8 + 63) / 64;
   const size_t per_wave = (size_t)g.jt * 1280 + act_dwords + d_rounds * 64;
   return (g.wk * per_wave + (exact ? 0 : (size_t)g.wk * g.rows * M)) * 4;
 }
@@ -198,14 +205,20 @@ int compute_units();
 // 23.43 -> 9.64).  Where the usual split fits, it stays: one lane per row
 // instead was 8 % slower at 16384 x 4096 and within 2 % at 16384 x 5120
 // and 28672 x 4096.
+// Whether every workgroup of an M-column launch with split g is resident at
+// once (LDS and wave slots over the workgroups a compute unit holds).
+bool fits_one_round(int M, const Geometry& g, int64_t rows_total) {
+  const size_t lds = lds_bytes(M, g, use_mf(M, g.lshift));
+  if (lds > (size_t)kMaxLdsBytesPerBlock) return false;
+  const int64_t per_cu = std::max<int64_t>(
+      1, std::min<int64_t>((int64_t)kMaxLdsBytesPerBlock / (int64_t)lds,
+                           wave_slots_per_cu(M) / g.wk));
+  return (rows_total + g.rows - 1) / g.rows <= compute_units() * per_cu;
+}
+
 Geometry columns_geometry(int64_t K, int M, int64_t rows_total) {
   const int64_t cus = compute_units();
-  auto one_round = [&](const Geometry& g) {
-    const size_t lds = lds_bytes(M, g, use_mf(M, g.lshift));
-    const int64_t per_cu = std::max<int64_t>(
-        1, std::min<int64_t>((int64_t)kMaxLdsBytesPerBlock / (int64_t)lds, kWaveSlotsPerCu / g.wk));
-    return (rows_total + g.rows - 1) / g.rows <= cus * per_cu;
-  };
+  auto one_round = [&](const Geometry& g) { return fits_one_round(M, g, rows_total); };
   auto workgroups = [&](const Geometry& g) { return (rows_total + g.rows - 1) / g.rows; };
   const Geometry g2 = pick_geometry(K, 2);
   if (workgroups(g2) >= kMinWorkgroupsForJ2) {
@@ -241,35 +254,62 @@ int compute_units() {
 
 }  // namespace
 
-// Each launch reads the whole matrix once, so the M columns should go through
-// as few launches as possible.  Up to seven columns, all of them go in one
-// launch whenever their LDS fits what keeps every workgroup resident in one
-// round (160 KiB over the workgroups per compute unit): at 16384 x 5120 (512
-// workgroups) M = 6 and 7 take 18.6 and 20.7 us in one launch against 22.4
-// and 24.5 us as 5+1 and 6+1 columns.  Otherwise (and always for eight
-// columns: one launch took 33.1 us against 27.3 us for 5+3, whether its
-// workgroups held one or two to a compute unit) launches of as many columns
-// as fit 64 KiB.
+// Each launch reads the whole matrix once, so the M columns should go
+// through as few launches as possible.  Two to eight columns run the
+// matrix-core form, all of them in one launch whenever some split of K lets
+// every workgroup of that launch be resident at once, else in launches of as
+// many columns as allow it.  (Before the matrix-core form took five to eight
+// columns, the dot4 kernel ran up to seven in one launch when their LDS fit
+// one round -- at 16384 x 5120 M = 6 and 7 took 18.6 and 20.7 us against
+// 22.4 and 24.5 us as 5+1 and 6+1 columns -- and eight as 5+3, 27.3 us
+// against 33.1 us in one launch, whose 157-register waves left one
+// workgroup per compute unit.)  Without a matrix-core split (more than 16
+// lanes per row): launches of as many dot4 columns as fit 64 KiB, or one
+// round.
 hipError_t launch_gemv(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
                        const float* d, int64_t M, float* y, hipStream_t stream) {
-  const Geometry g = M >= 2 && M <= 4 ? columns_geometry(K, (int)M, N) : geometry(K, M, N);
-  const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows));
-  const int64_t cus = compute_units();
-  const int64_t share = ((int64_t)grid.x + cus - 1) / cus;
-  const size_t one_round = (size_t)kMaxLdsBytesPerBlock / share;
-  auto bytes = [&](int c) { return lds_bytes(c, g, use_mf(c, g.lshift)); };
-  size_t cap = kMaxLdsBytes;
-  if (M <= 7 && bytes((int)M) <= one_round) cap = std::max(cap, one_round);
-  int cols = (int)M;
-  while (cols > 1 && bytes(cols) > cap) --cols;
-  for (int64_t m0 = 0; m0 < M; m0 += cols) {
-    const int mc = (int)std::min<int64_t>(cols, M - m0);
-    const bool mf = use_mf(mc, g.lshift);
+  auto launch = [&](int64_t m0, int mc, const Geometry& g, bool mf) {
+    const dim3 grid((uint32_t)((N + g.rows - 1) / g.rows));
     Params p{w, (int)N, (int)K, q + m0 * K, d + m0 * (K / 32), y + m0 * N,
              g.lshift, g.wk, g.J, nullptr, 0, nullptr, 1, 0, nullptr, nullptr, nullptr};
     hipLaunchKernelGGL(mf ? pick_mf(mc, g.jt) : pick_kernel(mc, g.jt), grid, dim3(64 * g.wk),
-                       bytes(mc), stream, p);
-    const hipError_t e = hipGetLastError();
+                       lds_bytes(mc, g, mf), stream, p);
+    return hipGetLastError();
+  };
+  if (M >= 2 && M <= 8) {
+    int cols = (int)M;
+    Geometry g = columns_geometry(K, cols, N);
+    while (cols > 2 && !(use_mf(cols, g.lshift) && fits_one_round(cols, g, N)))
+      g = columns_geometry(K, --cols, N);
+    if (use_mf(cols, g.lshift)) {
+      for (int64_t m0 = 0; m0 < M; m0 += cols) {
+        const int mc = (int)std::min<int64_t>(cols, M - m0);
+        if (mc >= 2) {
+          const Geometry gc = mc == cols ? g : columns_geometry(K, mc, N);
+          if (use_mf(mc, gc.lshift)) {
+            const hipError_t e = launch(m0, mc, gc, true);
+            if (e != hipSuccess) return e;
+            continue;
+          }
+        }
+        const hipError_t e = launch(m0, mc, geometry(K, mc, N), false);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
+  }
+  const Geometry g = geometry(K, M, N);
+  const int64_t cus = compute_units();
+  const int64_t grid = (N + g.rows - 1) / g.rows;
+  const int64_t share = (grid + cus - 1) / cus;
+  const size_t one_round = (size_t)kMaxLdsBytesPerBlock / share;
+  size_t cap = kMaxLdsBytes;
+  if (M <= 7 && lds_bytes((int)M, g) <= one_round) cap = std::max(cap, one_round);
+  int cols = (int)M;
+  while (cols > 1 && lds_bytes(cols, g) > cap) --cols;
+  for (int64_t m0 = 0; m0 < M; m0 += cols) {
+    const int mc = (int)std::min<int64_t>(cols, M - m0);
+    const hipError_t e = launch(m0, mc, g, false);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

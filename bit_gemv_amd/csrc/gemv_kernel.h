@@ -159,7 +159,7 @@ __device__ __forceinline__ void group_product(const uint32_t (&dw)[20],
   }
 }
 
-// Matrix-core form of group_product for two to four columns.  The int32 half
+// Matrix-core form of group_product for two to eight columns.  The int32 half
 // sums come from v_mfma_i32_4x4x4_16b_i8 instead of the lane's own dot4
 // chains: the instruction is sixteen independent 4x4x4 products, one per
 // quad of lanes (lanes 4q..4q+3); in quad q, lane 4q+i supplies row i of A
@@ -171,9 +171,11 @@ __device__ __forceinline__ void group_product(const uint32_t (&dw)[20],
 // steps over the words i = 0..3 of a half (weights i, 4+i, 8+i, 12+i, the
 // activations transposed to match) accumulate the half's int32 sum: the
 // same integers as half_dot, so the outputs are bit for bit those of
-// group_product.  `act` points at this lane's column's activations of the
-// group, `dact` at the group's block scales laid out [block][column] with
-// four columns per block.  Column slots past M (M < 4) compute unused sums.
+// group_product.  `act0` points at this lane's column's activations of the
+// group (column lane % 4), `act1` at those of column 4 + lane % 4 (five to
+// eight columns: a second quad of columns, a second set of products), and
+// `dact` at the group's block scales laid out [block][column] with four or
+// eight column slots per block.  Column slots past M compute unused sums.
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 // `start` is the accumulator's initial value (zero, or the bias below).
@@ -186,24 +188,40 @@ __device__ __forceinline__ v4i half_sums_mf(const uint32_t (&W)[4], const uint4&
   return s;
 }
 
-template <int M>
-__device__ __forceinline__ void group_product_mf(const uint32_t (&dw)[20], const uint32_t* act,
-                                                 const float* dact, float (&acc)[M],
-                                                 uint32_t& bad_lo, uint32_t& bad_hi) {
-  static_assert(M >= 2 && M <= 4, "one quad of columns");
-  auto load = [&](int jb, uint4& A0, uint4& A1, float4& d4) {
-    A0 = *reinterpret_cast<const uint4*>(act + jb * 8);
-    A1 = *reinterpret_cast<const uint4*>(act + jb * 8 + 4);
-    d4 = *reinterpret_cast<const float4*>(dact + jb * 4);
+// NQL: quads of column slots per block in the scale array (may exceed the
+// quads this call computes: a routed group of at most four columns in a
+// launch for more runs the first quad only).
+template <int M, int NQL = (M + 3) / 4>
+__device__ __forceinline__ void group_product_mf(const uint32_t (&dw)[20], const uint32_t* act0,
+                                                 const uint32_t* act1, const float* dact,
+                                                 float (&acc)[M], uint32_t& bad_lo,
+                                                 uint32_t& bad_hi) {
+  static_assert(M >= 2 && M <= 8, "one or two quads of columns");
+  constexpr int NQ = (M + 3) / 4;         // quads of columns: act0 = columns 0..3, act1 4..7
+  static_assert(NQL >= NQ, "the scale array holds every computed quad");
+  const uint32_t* act[2] = {act0, act1};
+  auto load = [&](int jb, uint4 (&A0)[NQ], uint4 (&A1)[NQ], float4 (&d4)[NQ]) {
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      A0[u] = *reinterpret_cast<const uint4*>(act[u] + jb * 8);
+      A1[u] = *reinterpret_cast<const uint4*>(act[u] + jb * 8 + 4);
+      d4[u] = *reinterpret_cast<const float4*>(dact + (jb * NQL + u) * 4);
+    }
   };
   // a block's activations are read one block ahead of its products
-  uint4 nA0, nA1;
-  float4 nd;
+  uint4 nA0[NQ], nA1[NQ];
+  float4 nd[NQ];
   load(0, nA0, nA1, nd);
 #pragma unroll
   for (int jb = 0; jb < 8; ++jb) {
-    const uint4 A0 = nA0, A1 = nA1;
-    const float4 d4 = nd;
+    uint4 A0[NQ], A1[NQ];
+    float4 d4[NQ];
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      A0[u] = nA0[u];
+      A1[u] = nA1[u];
+      d4[u] = nd[u];
+    }
     if (jb < 7) load(jb + 1, nA0, nA1, nd);
     uint32_t W0[4], W1[4], sc;
     float s0, s1;
@@ -217,13 +235,20 @@ __device__ __forceinline__ void group_product_mf(const uint32_t (&dw)[20], const
     // 2^22) and s0 * S0 = fma(s0, that, -1.5 * 2^23 * s0) is one exact
     // instruction (s0 has at most 4 significant bits, s0 * S0 at most 17):
     // the value the convert and the multiply give, one instruction fewer
-    const v4i S0 = half_sums_mf(W0, A0, v4i{0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000});
-    const v4i S1 = half_sums_mf(W1, A1);
-    const float nb0 = -12582912.0f * s0;
-    const float dm[4] = {d4.x, d4.y, d4.z, d4.w};
+    v4i S0[NQ], S1[NQ];
 #pragma unroll
-    for (int m = 0; m < M; ++m)
-      acc[m] = fmaf(dm[m], fmaf(s1, (float)S1[m], fmaf(s0, __int_as_float(S0[m]), nb0)), acc[m]);
+    for (int u = 0; u < NQ; ++u) {
+      S0[u] = half_sums_mf(W0, A0[u], v4i{0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000});
+      S1[u] = half_sums_mf(W1, A1[u]);
+    }
+    const float nb0 = -12582912.0f * s0;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int u = m >> 2, i = m & 3;
+      const float dm = i == 0 ? d4[u].x : i == 1 ? d4[u].y : i == 2 ? d4[u].z : d4[u].w;
+      acc[m] = fmaf(dm, fmaf(s1, (float)S1[u][i], fmaf(s0, __int_as_float(S0[u][i]), nb0)),
+                    acc[m]);
+    }
   }
 }
 
@@ -484,7 +509,7 @@ __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)"
 // precedes the final cross-wave sum.  M activation columns; MOE selects the
 // weight matrix through ids[blockIdx.y].  QH > 0: the quantizing form, each
 // lane quantizing QH (1 or 2) halves of the wave's activation slice.  MF:
-// the matrix-core form of two to four columns (group_product_mf), in which
+// the matrix-core form of two to eight columns (group_product_mf), in which
 // the four lanes of a quad are four rows at the same group: lane =
 // (slot / 4) * 4L + t * 4 + slot % 4, so it needs L <= 16.  A routed group
 // with fewer columns than M computes the missing ones from a repeat of its
@@ -494,7 +519,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
   constexpr bool QA = QH > 0;
   static_assert(QH >= 0 && QH <= 2, "one or two halves per lane");
   static_assert(!QA || (M == 1 && JT == 1), "the quantizing form is one column, one chunk");
-  static_assert(!MF || (M >= 2 && M <= 4 && !QA), "matrix-core form: 2..4 columns");
+  static_assert(!MF || (M >= 2 && M <= 8 && !QA), "matrix-core form: 2..8 columns");
   extern __shared__ uint32_t lds[];
   const int K = p.K, N = p.N;
   const int ls = p.lshift;
@@ -556,7 +581,7 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
   // their block scales (8 per group), each rounded up to whole 64-lane loads
   const int ag = p.J << ls;                     // activation groups of the wave
   const int n_pieces = M * ag * kGroupPieces;
-  constexpr int MD = MF ? 4 : M;                // column slots of the scale array
+  constexpr int MD = MF ? 4 * ((M + 3) / 4) : M;   // column slots of the scale array
   const int n_scales = MD * ag * 8;
   const int act_rounds = (n_pieces + 63) >> 6;
   const int d_rounds = (n_scales + 63) >> 6;
@@ -675,8 +700,11 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
         const int i = min(64 * r + lane, use_scales - 1);
         if constexpr (MF) {
           // [group][block][column slot]; slots past the last column re-read it
-          const int m = min(i & 3, ncols - 1);
-          dma4(p.d, (uint32_t)(4 * (token_of(m) * nb + group_of(i >> 5) * 8 + ((i >> 2) & 7))),
+          constexpr int kMDs = MD == 8 ? 3 : 2;
+          const int m = min(i & (MD - 1), ncols - 1);
+          dma4(p.d,
+               (uint32_t)(4 * (token_of(m) * nb + group_of(i >> (kMDs + 3)) * 8 +
+                               ((i >> kMDs) & 7))),
                m0d + 256 * r);
         } else {
           const int g = i >> 3;
@@ -732,9 +760,22 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
       load_chunk(wb + (int64_t)((((j + JT) * p.wk) + wave) << ls) * 80, co,
                  ring_m0 + 5120 * buf_i);
     const int lgl = (j << ls) + t;
-    if constexpr (MF)
-      group_product_mf<M>(buf, alds + min(lane & 3, ncols - 1) * act_stride + lgl * kGroupDwords,
-                          dlds + lgl * 32, acc, bad_lo, bad_hi);
+    if constexpr (MF) {
+      const uint32_t* act0 = alds + min(lane & 3, ncols - 1) * act_stride + lgl * kGroupDwords;
+      const uint32_t* act1 = alds + min(4 + (lane & 3), ncols - 1) * act_stride +
+                             lgl * kGroupDwords;
+      if constexpr (MOE && M > 4) {
+        // (uniform) a routed group of at most four columns: one quad of products
+        if (ncols <= 4) {
+          float(&acc4)[4] = *reinterpret_cast<float(*)[4]>(acc);
+          group_product_mf<4, 2>(buf, act0, act1, dlds + lgl * 8 * MD, acc4, bad_lo, bad_hi);
+        } else {
+          group_product_mf<M>(buf, act0, act1, dlds + lgl * 8 * MD, acc, bad_lo, bad_hi);
+        }
+      } else {
+        group_product_mf<M>(buf, act0, act1, dlds + lgl * 8 * MD, acc, bad_lo, bad_hi);
+      }
+    }
     else
       group_product<M, (M <= 4) && (!MOE || M == 1)>(buf, alds + lgl * kGroupDwords, act_stride,
                                                     dlds + lgl * 8, ag * 8, acc, bad_lo, bad_hi,

@@ -6,6 +6,8 @@ namespace gemv_detail {
 
 GemvFn pick_m5(int jt) { return pick<5, false>(jt); }
 GemvFn pick_m6(int jt) { return pick<6, false>(jt); }
+GemvFn pick_m5_mf(int jt) { return pick<5, false, true>(jt); }
+GemvFn pick_m6_mf(int jt) { return pick<6, false, true>(jt); }
 
 }  // namespace gemv_detail
 }  // namespace rfp2

@@ -6,6 +6,8 @@ namespace gemv_detail {
 
 GemvFn pick_m7(int jt) { return pick<7, false>(jt); }
 GemvFn pick_m8(int jt) { return pick<8, false>(jt); }
+GemvFn pick_m7_mf(int jt) { return pick<7, false, true>(jt); }
+GemvFn pick_m8_mf(int jt) { return pick<8, false, true>(jt); }
 
 }  // namespace gemv_detail
 }  // namespace rfp2

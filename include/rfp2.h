@@ -339,7 +339,7 @@ rfp2_status rfp2_read_ceiling(const uint8_t* buf, int64_t bytes, uint32_t magic,
  * M * N * (K/32) <= 2^40; w 2-byte aligned, q 4-byte aligned.
  *
  * rfp2_debug_half_sums_mf: the same int32 half sums as computed by the
- * GEMV's matrix-core form of two to four columns (v_mfma_i32_4x4x4_16b_i8
+ * GEMV's matrix-core form of two to eight columns (v_mfma_i32_4x4x4_16b_i8
  * over quads of four rows at one 8-block group, one column's activations per
  * lane; "03 · Runtime": the half's int8 products summed in int32 before any
  * scale), sums_out [M][N][K/32][2] int32 as rfp2_debug_half_dots.  Requires
