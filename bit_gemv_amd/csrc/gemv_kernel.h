@@ -277,7 +277,7 @@ __device__ __forceinline__ ChunkOffsets chunk_offsets(int lane, int lshift,
     const int r = (c >> lshift) / 5;
     const int col = c - r * seg;
     const int rr = min(r, N - 1 - row0);       // clamp rows past the end
-    o.off[k] = rr * row_bytes + col * 16;
+    o.off[k] = (int)__umul24((uint32_t)rr, (uint32_t)row_bytes) + col * 16;  // both < 2^24
   }
   return o;
 }
@@ -605,8 +605,10 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
   uint32_t* alds = wlds + JT * 1280;
   float* dlds = reinterpret_cast<float*>(alds + act_dwords);
   const int nb = K >> 5;
+  // (24-bit multiplies, full rate: every index here is below 2^24, K below 2^16)
   auto group_of = [&](int lgl) {
-    return (((lgl >> ls) * p.wk + wave) << ls) + (lgl & (L - 1));
+    return (int)((__umul24((uint32_t)(lgl >> ls), (uint32_t)p.wk) + wave) << ls) +
+           (lgl & (L - 1));
   };
   // token of a lane-dependent column index: lane c of tok_lanes holds
   // col_tok[c], read back with a lane shuffle (no indexed register array,
@@ -677,23 +679,39 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
     // rounding slack re-read the first piece.
     {
       const uint32_t m0 = lds_m0(alds);
-      // the wave's groups per column, ag = J * L: a shift when J is a power
-      // of two (uniform)
+      // the wave's groups per column, ag = J * L: column of a local group g
+      // by a shift when ag is a power of two (uniform), else as a float
+      // quotient, exact for g < 2^21 ((g + 1/2) / ag is at least 1 / (2 ag)
+      // from an integer; the reciprocal, within one ulp, and the rounded
+      // product move it by less than 1.5 * 2^-23 of itself)
       const bool ag_pow2 = (ag & (ag - 1)) == 0;
       const int ag_shift = __builtin_ctz(ag);
+      const float inv_ag = __builtin_amdgcn_rcpf((float)ag);
+      auto col_of = [&](int g) {
+        return M == 1 ? 0 : ag_pow2 ? g >> ag_shift : (int)(((float)g + 0.5f) * inv_ag);
+      };
+      // round r loads LDS piece pc = 64 r + lane: g = pc / 17 and
+      // piece = pc % 17 are stepped from round to round (64 = 3 * 17 + 13)
+      int g = (lane * 241) >> 12;                 // lane / 17 for lane < 64
+      int piece = lane - kGroupPieces * g;
       for (int r = 0; r < use_act_rounds; ++r) {
-        const int pc = 64 * r + lane;
-        const int g = pc / kGroupPieces, piece = pc - g * kGroupPieces;
         const bool used = piece < 16 && g < ncols * ag;
         const int gu = used ? g : 0;
-        const int m = M == 1 ? 0 : ag_pow2 ? gu >> ag_shift : gu / ag;
-        const int lgl = gu - m * ag;
+        const int m = col_of(gu);
+        const int lgl = gu - (int)__umul24((uint32_t)m, (uint32_t)ag);
         // the token lookup is a lane shuffle: every lane must take part (a
         // lane left out of it reads as 0 to the others)
         const int tok = token_of(m);
         const uint32_t off =
-            used ? (uint32_t)(tok * K + (group_of(lgl) * 16 + piece) * 16) : 0u;
-        if (!EXACT || pc < n_pieces) dma16(p.q, off, m0 + 1024 * r);
+            used ? __umul24((uint32_t)tok, (uint32_t)K) + (uint32_t)((group_of(lgl) * 16 + piece) * 16)
+                 : 0u;
+        if (!EXACT || 64 * r + lane < n_pieces) dma16(p.q, off, m0 + 1024 * r);
+        piece += 64 - 3 * kGroupPieces;
+        g += 3;
+        if (piece >= kGroupPieces) {
+          piece -= kGroupPieces;
+          ++g;
+        }
       }
       const uint32_t m0d = lds_m0(dlds);
       for (int r = 0; r < use_d_rounds; ++r) {
@@ -703,14 +721,16 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
           constexpr int kMDs = MD == 8 ? 3 : 2;
           const int m = min(i & (MD - 1), ncols - 1);
           dma4(p.d,
-               (uint32_t)(4 * (token_of(m) * nb + group_of(i >> (kMDs + 3)) * 8 +
-                               ((i >> kMDs) & 7))),
+               4 * (__umul24((uint32_t)token_of(m), (uint32_t)nb) +
+                    (uint32_t)(group_of(i >> (kMDs + 3)) * 8 + ((i >> kMDs) & 7))),
                m0d + 256 * r);
         } else {
-          const int g = i >> 3;
-          const int m = M == 1 ? 0 : ag_pow2 ? g >> ag_shift : g / ag;
-          const int lgl = g - m * ag;
-          dma4(p.d, (uint32_t)(4 * (token_of(m) * nb + group_of(lgl) * 8 + (i & 7))),
+          const int gi = i >> 3;
+          const int m = col_of(gi);
+          const int lgl = gi - (int)__umul24((uint32_t)m, (uint32_t)ag);
+          dma4(p.d,
+               4 * (__umul24((uint32_t)token_of(m), (uint32_t)nb) +
+                    (uint32_t)(group_of(lgl) * 8 + (i & 7))),
                m0d + 256 * r);
         }
       }
@@ -721,15 +741,27 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
     wait_chunks(JT);
 
     // transpose each half's 16 activations in place into the lane order of
-    // the expanded weights
-    for (int pc = lane; pc < use_pieces; pc += 64) {
-      if (pc % kGroupPieces == 16) continue;
-      uint4* a = reinterpret_cast<uint4*>(alds) + pc;
-      const uint4 x = *a;
-      const uint32_t X[4] = {x.x, x.y, x.z, x.w};
-      uint32_t A[4];
-      transpose_half(X, A);
-      *a = make_uint4(A[0], A[1], A[2], A[3]);
+    // the expanded weights: every piece the loads above wrote (pad pieces and
+    // the rounding slack hold copies of a first piece that nothing reads),
+    // two rounds at a time so that their LDS reads overlap
+    {
+      uint4* const base = reinterpret_cast<uint4*>(alds);
+      auto transpose_piece = [&](const uint4& x) {
+        const uint32_t X[4] = {x.x, x.y, x.z, x.w};
+        uint32_t A[4];
+        transpose_half(X, A);
+        return make_uint4(A[0], A[1], A[2], A[3]);
+      };
+      for (int r = 0; r < use_act_rounds; r += 2) {
+        const int pc0 = 64 * r + lane, pc1 = pc0 + 64;
+        const bool ok0 = !EXACT || pc0 < n_pieces;
+        const bool ok1 = r + 1 < use_act_rounds && (!EXACT || pc1 < n_pieces);
+        uint4 x0 = make_uint4(0, 0, 0, 0), x1 = x0;
+        if (ok0) x0 = base[pc0];
+        if (ok1) x1 = base[pc1];
+        if (ok0) base[pc0] = transpose_piece(x0);
+        if (ok1) base[pc1] = transpose_piece(x1);
+      }
     }
   }
 
