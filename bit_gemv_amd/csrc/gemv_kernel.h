@@ -319,10 +319,16 @@ __device__ __forceinline__ void load_chunk(const uint8_t* base, const ChunkOffse
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // Quantizing form: the lane's 16 fp32 activations (64 bytes at abase + aoff)
-// into registers, then one weight chunk (as load_chunk), then a wait for the
-// activations only.  One asm statement, so that the registers the loads fill
-// are not touched before the wait (the outputs are early-clobber: no input
-// shares a register with them while the loads are in flight).
+// into registers, a workgroup barrier (every wave's activation loads are
+// then queued ahead of the workgroup's weight loads: a compute unit returns
+// vector loads in order, so an activation load, an L2 hit, issued after other
+// waves' weight loads waits for their HBM data; one token at 16384 x 5120,
+// 4096 x 4096, 4096 x 14336, 65536 x 5120: 8.84, 4.32, 7.64, 27.78 -> 8.54,
+// 4.06, 7.21, 26.60 us), then one weight chunk (as load_chunk), then a wait
+// for the activations only.  One asm statement, so
+// that the registers the loads fill are not touched before the wait (the
+// outputs are early-clobber: no input shares a register with them while the
+// loads are in flight).  Every wave of the workgroup runs it exactly once.
 __device__ __forceinline__ void load_acts_and_chunk(const float* abase, uint32_t aoff,
                                                     const uint8_t* wbase, const ChunkOffsets& o,
                                                     uint32_t m0v, v4f (&x)[4]) {
@@ -331,6 +337,7 @@ __device__ __forceinline__ void load_acts_and_chunk(const float* abase, uint32_t
       "global_load_dwordx4 %1, %4, %5 offset:16\n\t"
       "global_load_dwordx4 %2, %4, %5 offset:32\n\t"
       "global_load_dwordx4 %3, %4, %5 offset:48\n\t"
+      "s_barrier\n\t"
       "s_mov_b32 m0, %11\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, %12\n\t"
       "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %7, %12\n\t"
       "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %8, %12\n\t"
@@ -344,7 +351,8 @@ __device__ __forceinline__ void load_acts_and_chunk(const float* abase, uint32_t
 }
 
 // The same for two halves per lane: 2 x 16 fp32 activations at abase + aoff0
-// and abase + aoff1, then the weight chunk, then a wait for the activations.
+// and abase + aoff1, the barrier, then the weight chunk, then a wait for the
+// activations.
 __device__ __forceinline__ void load_acts2_and_chunk(const float* abase, uint32_t aoff0,
                                                      uint32_t aoff1, const uint8_t* wbase,
                                                      const ChunkOffsets& o, uint32_t m0v,
@@ -358,6 +366,7 @@ __device__ __forceinline__ void load_acts2_and_chunk(const float* abase, uint32_
       "global_load_dwordx4 %5, %9, %10 offset:16\n\t"
       "global_load_dwordx4 %6, %9, %10 offset:32\n\t"
       "global_load_dwordx4 %7, %9, %10 offset:48\n\t"
+      "s_barrier\n\t"
       "s_mov_b32 m0, %16\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %11, %17\n\t"
       "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %12, %17\n\t"
       "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %13, %17\n\t"
@@ -735,6 +744,17 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
         }
       }
     }
+    // Routed form: every wave's activation loads go ahead of the
+    // workgroup's weight loads (vector loads return in order on a compute
+    // unit: an activation load queued behind other waves' weight loads waits
+    // for their HBM data).  Uniform: every wave of a workgroup that gets here
+    // reaches it once (a workgroup that leaves early leaves as a whole).
+    // 128 experts of 1536 x 4096, top-8, half of each token's experts
+    // shared, T = 2, 3, 4: 8.89, 11.60, 12.35 -> 8.69, 10.87, 12.08 us; the
+    // dense loaded form, whose median wait for its activations at 16384 x
+    // 5120, M = 4 fell from 2.7 to 1.6 us, was within 1 % at most sizes but
+    // 4 % slower at 4096 x 14336 and goes without it.
+    if constexpr (MOE) __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int j = 0; j < JT; ++j)                 // J is a multiple of JT
       load_chunk(wb + (int64_t)((j * p.wk + wave) << ls) * 80, co, ring_m0 + 5120 * j);
