@@ -353,23 +353,45 @@ __device__ __forceinline__ void store_act_block(uint4 lo_half, uint4 hi_half, fl
   st.ad[b][m] = d;
 }
 
-// Block b of the stage against this wave's A operands: both token tiles
-// (the second only when the tile holds more than 32 slots).
-__device__ __forceinline__ void moe_block(const MoeStage& st, int b, int lane, v8h a0, v8h a1,
-                                          bool two, v16f (&acc)[2]) {
+// Block b of the stage: this lane's B operands (both steps) and activation
+// scale in each token tile (the second only when the tile holds more than 32
+// slots), read from LDS one block ahead of their products.
+struct MoeB {
+  v8h b0[2], b1[2];
+  float dd[2];
+};
+
+__device__ __forceinline__ void moe_b(const MoeStage& st, int b, int lane, bool two, MoeB& o) {
   const int kh = lane >> 5;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     if (t == 1 && !two) break;
     const int m = t * 32 + (lane & 31);
     const uint8_t* row = st.ah + m * kMoeActRow + b * 64 + kh * 16;
-    const v8h b0 = *reinterpret_cast<const v8h*>(row);
-    const v8h b1 = *reinterpret_cast<const v8h*>(row + 32);
-    const float dd = st.ad[b][m];
-    v16f c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, v16f{}, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, c, 0, 0, 0);
+    o.b0[t] = *reinterpret_cast<const v8h*>(row);
+    o.b1[t] = *reinterpret_cast<const v8h*>(row + 32);
+    o.dd[t] = st.ad[b][m];
+  }
+}
+
+// The block's sums (two 16-k steps) in each token tile ...
+__device__ __forceinline__ void moe_mma(v8h a0, v8h a1, const MoeB& B, bool two, v16f (&c)[2]) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[t][r] = fmaf(dd, c[r], acc[t][r]);
+  for (int t = 0; t < 2; ++t) {
+    if (t == 1 && !two) break;
+    c[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, B.b0[t], v16f{}, 0, 0, 0);
+    c[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, B.b1[t], c[t], 0, 0, 0);
+  }
+}
+
+// ... rescaled by the activation scale and added to acc.
+__device__ __forceinline__ void moe_scale(const MoeB& B, const v16f (&c)[2], bool two,
+                                          v16f (&acc)[2]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (t == 1 && !two) break;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = fmaf(B.dd[t], c[t][r], acc[t][r]);
   }
 }
 
@@ -423,27 +445,31 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_kernel(GemmF16Params p) {
     if (two) store_act_block(ap.q2, ap.q3, ap.d1, sm, am, ab + 1);
     load_acts(ap, qrow, drow, kb_next, two);
     __syncthreads();
+    // Software-pipelined over the stage's 8 blocks: block b's products are
+    // issued, then block b + 1's B operands are read and its A operands
+    // decoded while they run, then block b is rescaled (its products are
+    // only read once the next block's decode has covered their latency).
+    MoeB bc, bn;
+    v16f c[2];
     v8h a0, a1;
+    moe_b(sm, 0, lane, two, bc);
     decode_half<0>(w0, kh, a0, a1);
-    moe_block(sm, 0, lane, a0, a1, two, acc);
-    decode_half<1>(w0, kh, a0, a1);
-    load_pair(w0, wrow, kb_next + 0);
-    moe_block(sm, 1, lane, a0, a1, two, acc);
-    decode_half<0>(w1, kh, a0, a1);
-    moe_block(sm, 2, lane, a0, a1, two, acc);
-    decode_half<1>(w1, kh, a0, a1);
-    load_pair(w1, wrow, kb_next + 2);
-    moe_block(sm, 3, lane, a0, a1, two, acc);
-    decode_half<0>(w2, kh, a0, a1);
-    moe_block(sm, 4, lane, a0, a1, two, acc);
-    decode_half<1>(w2, kh, a0, a1);
-    load_pair(w2, wrow, kb_next + 4);
-    moe_block(sm, 5, lane, a0, a1, two, acc);
-    decode_half<0>(w3, kh, a0, a1);
-    moe_block(sm, 6, lane, a0, a1, two, acc);
-    decode_half<1>(w3, kh, a0, a1);
-    load_pair(w3, wrow, kb_next + 6);
-    moe_block(sm, 7, lane, a0, a1, two, acc);
+#define RFP2_MOE_STEP(b, NEXT)                                  \
+    moe_mma(a0, a1, bc, two, c);                                \
+    if ((b) < 7) moe_b(sm, (b) + 1, lane, two, bn);             \
+    NEXT;                                                       \
+    moe_scale(bc, c, two, acc);                                 \
+    bc = bn;                                                    \
+    __builtin_amdgcn_sched_barrier(0);
+    RFP2_MOE_STEP(0, decode_half<1>(w0, kh, a0, a1); load_pair(w0, wrow, kb_next + 0))
+    RFP2_MOE_STEP(1, decode_half<0>(w1, kh, a0, a1))
+    RFP2_MOE_STEP(2, decode_half<1>(w1, kh, a0, a1); load_pair(w1, wrow, kb_next + 2))
+    RFP2_MOE_STEP(3, decode_half<0>(w2, kh, a0, a1))
+    RFP2_MOE_STEP(4, decode_half<1>(w2, kh, a0, a1); load_pair(w2, wrow, kb_next + 4))
+    RFP2_MOE_STEP(5, decode_half<0>(w3, kh, a0, a1))
+    RFP2_MOE_STEP(6, decode_half<1>(w3, kh, a0, a1); load_pair(w3, wrow, kb_next + 6))
+    RFP2_MOE_STEP(7, (void)0)
+#undef RFP2_MOE_STEP
   }
 
   // lane -> token, register r -> row; rows n..n+3 of a register group are
