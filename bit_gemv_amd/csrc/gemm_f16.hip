@@ -447,13 +447,14 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_kernel(GemmF16Params p) {
   // read once the next block's decode has covered their latency).  A
   // scheduling barrier per block keeps the compiler from hoisting further
   // (without it the kernel took 256 registers and spilled).
-#define RFP2_MOE_STEP(ST, b, NEXT)                              \
-    moe_mma(a0, a1, bc, two, c);                                \
-    if ((b) < kMoeKB - 1) moe_b(ST, (b) + 1, lane, two, bn);    \
+#define RFP2_MOE_STEP(ST, b, BC, BN, NEXT)                      \
+    moe_mma(a0, a1, BC, TWO, c);                                \
+    if ((b) < kMoeKB - 1) moe_b(ST, (b) + 1, lane, TWO, BN);    \
     NEXT;                                                       \
-    moe_scale(bc, c, two, acc);                                 \
-    bc = bn;                                                    \
+    moe_scale(BC, c, TWO, acc);                                 \
     __builtin_amdgcn_sched_barrier(0);
+  // (the B operands alternate between two named sets, so that no block
+  // copies them from one to the other)
 #define RFP2_MOE_STAGE(S, CUR, NXT, W0, W1)                                          \
   {                                                                                  \
     const int kb2 = min((S) + 2, nst - 1) * kMoeKB;    /* past the end: re-read */   \
@@ -462,20 +463,34 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_kernel(GemmF16Params p) {
       if ((S) + 2 < nst) load_acts(ap, qrow, drow, ((S) + 2) * kMoeKB);              \
     }                                                                                \
     __builtin_amdgcn_sched_barrier(0);                                               \
-    MoeB bc, bn;                                                                     \
+    MoeB bx, by;                                                                     \
     v16f c[2];                                                                       \
     v8h a0, a1;                                                                      \
-    moe_b(CUR, 0, lane, two, bc);                                                    \
+    moe_b(CUR, 0, lane, TWO, bx);                                                    \
     decode_half<0>(W0, kh, a0, a1);                                                  \
-    RFP2_MOE_STEP(CUR, 0, decode_half<1>(W0, kh, a0, a1); load_pair(W0, wrow, kb2))  \
-    RFP2_MOE_STEP(CUR, 1, decode_half<0>(W1, kh, a0, a1))                            \
-    RFP2_MOE_STEP(CUR, 2, decode_half<1>(W1, kh, a0, a1); load_pair(W1, wrow, kb2 + 2)) \
-    RFP2_MOE_STEP(CUR, 3, (void)0)                                                   \
+    RFP2_MOE_STEP(CUR, 0, bx, by, decode_half<1>(W0, kh, a0, a1); load_pair(W0, wrow, kb2)) \
+    RFP2_MOE_STEP(CUR, 1, by, bx, decode_half<0>(W1, kh, a0, a1))                   \
+    RFP2_MOE_STEP(CUR, 2, bx, by, decode_half<1>(W1, kh, a0, a1); load_pair(W1, wrow, kb2 + 2)) \
+    RFP2_MOE_STEP(CUR, 3, by, bx, (void)0)                                          \
     __syncthreads();                                                                 \
   }
-  for (int s = 0; s < nst; s += 2) {            // nst is even: K % 256 == 0
-    RFP2_MOE_STAGE(s, sm[0], sm[1], wa0, wa1)
-    RFP2_MOE_STAGE(s + 1, sm[1], sm[0], wb0, wb1)
+  // one copy of the loop per tile kind (one or two 32-token MFMA tiles), so
+  // that no block branches on it: with a branch per block the compiler
+  // copied the 32 accumulator registers back and forth around it
+  if (two) {
+#define TWO true
+    for (int s = 0; s < nst; s += 2) {          // nst is even: K % 256 == 0
+      RFP2_MOE_STAGE(s, sm[0], sm[1], wa0, wa1)
+      RFP2_MOE_STAGE(s + 1, sm[1], sm[0], wb0, wb1)
+    }
+#undef TWO
+  } else {
+#define TWO false
+    for (int s = 0; s < nst; s += 2) {
+      RFP2_MOE_STAGE(s, sm[0], sm[1], wa0, wa1)
+      RFP2_MOE_STAGE(s + 1, sm[1], sm[0], wb0, wb1)
+    }
+#undef TWO
   }
 #undef RFP2_MOE_STAGE
 #undef RFP2_MOE_STEP

@@ -323,9 +323,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // then queued ahead of the workgroup's weight loads: a compute unit returns
 // vector loads in order, so an activation load, an L2 hit, issued after other
 // waves' weight loads waits for their HBM data; one token at 16384 x 5120,
-// 4096 x 4096, 4096 x 14336, 65536 x 5120: 8.84, 4.32, 7.64, 27.78 -> 8.54,
-// 4.06, 7.21, 26.60 us), then one weight chunk (as load_chunk), then a wait
-// for the activations only.  One asm statement, so
+// 4096 x 4096, 4096 x 14336, 512 x 2048, alternating timings: 8.32, 4.29,
+// 7.52, 4.03 -> 8.11, 4.07, 7.08, 3.88 us), then one weight chunk (as
+// load_chunk), then a wait for the activations only.  One asm statement, so
 // that the registers the loads fill are not touched before the wait (the
 // outputs are early-clobber: no input shares a register with them while the
 // loads are in flight).  Every wave of the workgroup runs it exactly once.
@@ -744,17 +744,6 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
         }
       }
     }
-    // Routed form: every wave's activation loads go ahead of the
-    // workgroup's weight loads (vector loads return in order on a compute
-    // unit: an activation load queued behind other waves' weight loads waits
-    // for their HBM data).  Uniform: every wave of a workgroup that gets here
-    // reaches it once (a workgroup that leaves early leaves as a whole).
-    // 128 experts of 1536 x 4096, top-8, half of each token's experts
-    // shared, T = 2, 3, 4: 8.89, 11.60, 12.35 -> 8.69, 10.87, 12.08 us; the
-    // dense loaded form, whose median wait for its activations at 16384 x
-    // 5120, M = 4 fell from 2.7 to 1.6 us, was within 1 % at most sizes but
-    // 4 % slower at 4096 x 14336 and goes without it.
-    if constexpr (MOE) __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int j = 0; j < JT; ++j)                 // J is a multiple of JT
       load_chunk(wb + (int64_t)((j * p.wk + wave) << ls) * 80, co, ring_m0 + 5120 * j);
