@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_kernel(GemmF16Params p) {
 constexpr int kMoeWaves = 4;
 constexpr int kMoeRows = 32 * kMoeWaves;      // weight rows per workgroup
 constexpr int kMoeTokens = 64;                // slots per tile: two 32-token MFMA tiles
-constexpr int kMoeKB = 4;                     // blocks per activation stage (two buffers)
+constexpr int kMoeKB = 8;                     // blocks per activation stage
 constexpr int kMoeActRow = kMoeKB * 64 + 16;  // fp16 bytes of one token's stage (+ pad)
 
 struct __align__(16) MoeStage {
@@ -313,21 +313,27 @@ __device__ __forceinline__ void load_pair(WPair& w, const uint8_t* row, int kb) 
   w.d4 = src[4];
 }
 
-// One block of a stage's activations for one thread: token t % 64, block
-// t / 64 of the stage; in a tile of at most 32 slots, token t % 32 and block
-// t / 32 (threads 128 .. 255 idle).  Staging the tile's real tokens only
-// keeps those tiles' conversion work at half.
-struct ActBlock {
-  uint4 q0, q1;
-  float d0;
+// One stage of activations for one thread: token t % 64, blocks 2 (t / 64)
+// and 2 (t / 64) + 1 of the stage; in a tile of at most 32 slots, token
+// t % 32 and block t / 32 only (q2, q3, d1 unused).  Staging the tile's real
+// tokens only halves those tiles' conversion work.
+struct ActPair {
+  uint4 q0, q1, q2, q3;
+  float d0, d1;
 };
 
-__device__ __forceinline__ void load_acts(ActBlock& a, const int8_t* qrow, const float* drow,
+template <bool TWO>
+__device__ __forceinline__ void load_acts(ActPair& a, const int8_t* qrow, const float* drow,
                                           int kb) {
   const uint4* src = reinterpret_cast<const uint4*>(qrow + (int64_t)kb * 32);
   a.q0 = src[0];
   a.q1 = src[1];
   a.d0 = drow[kb];
+  if (TWO) {
+    a.q2 = src[2];
+    a.q3 = src[3];
+    a.d1 = drow[kb + 1];
+  }
 }
 
 __device__ __forceinline__ void store_act_block(uint4 lo_half, uint4 hi_half, float d,
@@ -389,7 +395,7 @@ __device__ __forceinline__ void moe_scale(const MoeB& B, const v16f (&c)[2], boo
 }
 
 __global__ __launch_bounds__(256, 2) void moe_gemm_kernel(GemmF16Params p) {
-  __shared__ MoeStage sm[2];
+  __shared__ MoeStage sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -414,85 +420,69 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_kernel(GemmF16Params p) {
   const int n = n0 + wave * 32 + (lane & 31);
   const uint8_t* wrow = p.w + (int64_t)e * N * row_bytes + (int64_t)(n < N ? n : 0) * row_bytes;
   // (consecutive lanes take consecutive tokens: their 16-byte LDS stores,
-  // 272 bytes apart, fall on distinct banks).
+  // 528 bytes apart, fall on distinct banks).  A tile of at most 32 slots
+  // stages only its first 32 token rows: one block per thread per stage.
   const int am = two ? tid & 63 : tid & 31;
-  const int ab = two ? tid >> 6 : tid >> 5;
-  const bool act_ok = two || tid < 128;       // this thread stages a block
+  const int ab = two ? 2 * (tid >> 6) : tid >> 5;
   const int token = p.order[start + min(am, rows - 1)] / p.top_k;
   const int8_t* qrow = p.q + (int64_t)token * K + ab * 32;
   const float* drow = p.d + (int64_t)token * nb + ab;
 
-  // Two LDS stage buffers: stage s reads buffer s % 2 while the activations
-  // of stage s + 1 (loaded during stage s - 1) go into the other one and
-  // those of stage s + 2 are loaded; one barrier per stage.  The weights are
-  // read two stages (8 blocks) ahead: pairs wa0, wa1 serve the even stages,
-  // wb0, wb1 the odd ones, each reloaded for stage s + 2 once decoded.
   v16f acc[2] = {v16f{}, v16f{}};
-  WPair wa0, wa1, wb0, wb1;
-  load_pair(wa0, wrow, 0);
-  load_pair(wa1, wrow, 2);
-  load_pair(wb0, wrow, 4);
-  load_pair(wb1, wrow, 6);
-  ActBlock ap;
-  if (act_ok) {
-    load_acts(ap, qrow, drow, 0);
-    store_act_block(ap.q0, ap.q1, ap.d0, sm[0], am, ab);
-    load_acts(ap, qrow, drow, kMoeKB);
-  }
-  __syncthreads();
+  WPair w0, w1, w2, w3;                         // the stage's four pairs of blocks
+  load_pair(w0, wrow, 0);
+  load_pair(w1, wrow, 2);
+  load_pair(w2, wrow, 4);
+  load_pair(w3, wrow, 6);
+  ActPair ap;
 
-  // Each stage is software-pipelined over its 4 blocks: block b's products
-  // are issued, then block b + 1's B operands are read and its A operands
-  // decoded while they run, then block b is rescaled (its products are only
-  // read once the next block's decode has covered their latency).  A
-  // scheduling barrier per block keeps the compiler from hoisting further
-  // (without it the kernel took 256 registers and spilled).
-#define RFP2_MOE_STEP(ST, b, BC, BN, NEXT)                      \
+  // Per stage: this stage's activations (loaded during the previous one) go
+  // into LDS between two barriers and the next stage's are loaded; then the
+  // 8 blocks, software-pipelined: block b's products are issued, then block
+  // b + 1's B operands are read and its A operands decoded while they run,
+  // then block b is rescaled (its products are only read once the next
+  // block's decode has covered their latency).  The B operands alternate
+  // between two named sets, so that no block copies them, and a scheduling
+  // barrier per block keeps the compiler from hoisting further (without it
+  // the kernel took 256 registers and spilled).  One copy of the loop per
+  // tile kind (one or two 32-token MFMA tiles), so that no block branches on
+  // it: with a branch per block the compiler copied the 32 accumulator
+  // registers back and forth around it.
+#define RFP2_MOE_STEP(TWO, b, BC, BN, NEXT)                     \
     moe_mma(a0, a1, BC, TWO, c);                                \
-    if ((b) < kMoeKB - 1) moe_b(ST, (b) + 1, lane, TWO, BN);    \
+    if ((b) < kMoeKB - 1) moe_b(sm, (b) + 1, lane, TWO, BN);    \
     NEXT;                                                       \
     moe_scale(BC, c, TWO, acc);                                 \
     __builtin_amdgcn_sched_barrier(0);
-  // (the B operands alternate between two named sets, so that no block
-  // copies them from one to the other)
-#define RFP2_MOE_STAGE(S, CUR, NXT, W0, W1)                                          \
-  {                                                                                  \
-    const int kb2 = min((S) + 2, nst - 1) * kMoeKB;    /* past the end: re-read */   \
-    if (act_ok && (S) + 1 < nst) {                                                   \
-      store_act_block(ap.q0, ap.q1, ap.d0, NXT, am, ab);                             \
-      if ((S) + 2 < nst) load_acts(ap, qrow, drow, ((S) + 2) * kMoeKB);              \
-    }                                                                                \
-    __builtin_amdgcn_sched_barrier(0);                                               \
+#define RFP2_MOE_LOOP(TWO)                                                           \
+  load_acts<TWO>(ap, qrow, drow, 0);                                                 \
+  for (int s = 0; s < nst; ++s) {                                                    \
+    const int kb_next = min(s + 1, nst - 1) * kMoeKB;   /* past the end: re-read */  \
+    __syncthreads();                          /* every wave is done with sm */       \
+    store_act_block(ap.q0, ap.q1, ap.d0, sm, am, ab);                                \
+    if (TWO) store_act_block(ap.q2, ap.q3, ap.d1, sm, am, ab + 1);                   \
+    load_acts<TWO>(ap, qrow, drow, kb_next);                                         \
+    __syncthreads();                                                                 \
     MoeB bx, by;                                                                     \
     v16f c[2];                                                                       \
     v8h a0, a1;                                                                      \
-    moe_b(CUR, 0, lane, TWO, bx);                                                    \
-    decode_half<0>(W0, kh, a0, a1);                                                  \
-    RFP2_MOE_STEP(CUR, 0, bx, by, decode_half<1>(W0, kh, a0, a1); load_pair(W0, wrow, kb2)) \
-    RFP2_MOE_STEP(CUR, 1, by, bx, decode_half<0>(W1, kh, a0, a1))                   \
-    RFP2_MOE_STEP(CUR, 2, bx, by, decode_half<1>(W1, kh, a0, a1); load_pair(W1, wrow, kb2 + 2)) \
-    RFP2_MOE_STEP(CUR, 3, by, bx, (void)0)                                          \
-    __syncthreads();                                                                 \
+    moe_b(sm, 0, lane, TWO, bx);                                                     \
+    decode_half<0>(w0, kh, a0, a1);                                                  \
+    RFP2_MOE_STEP(TWO, 0, bx, by, decode_half<1>(w0, kh, a0, a1); load_pair(w0, wrow, kb_next + 0)) \
+    RFP2_MOE_STEP(TWO, 1, by, bx, decode_half<0>(w1, kh, a0, a1))                   \
+    RFP2_MOE_STEP(TWO, 2, bx, by, decode_half<1>(w1, kh, a0, a1); load_pair(w1, wrow, kb_next + 2)) \
+    RFP2_MOE_STEP(TWO, 3, by, bx, decode_half<0>(w2, kh, a0, a1))                   \
+    RFP2_MOE_STEP(TWO, 4, bx, by, decode_half<1>(w2, kh, a0, a1); load_pair(w2, wrow, kb_next + 4)) \
+    RFP2_MOE_STEP(TWO, 5, by, bx, decode_half<0>(w3, kh, a0, a1))                   \
+    RFP2_MOE_STEP(TWO, 6, bx, by, decode_half<1>(w3, kh, a0, a1); load_pair(w3, wrow, kb_next + 6)) \
+    RFP2_MOE_STEP(TWO, 7, by, bx, (void)0)                                          \
   }
-  // one copy of the loop per tile kind (one or two 32-token MFMA tiles), so
-  // that no block branches on it: with a branch per block the compiler
-  // copied the 32 accumulator registers back and forth around it
   if (two) {
-#define TWO true
-    for (int s = 0; s < nst; s += 2) {          // nst is even: K % 256 == 0
-      RFP2_MOE_STAGE(s, sm[0], sm[1], wa0, wa1)
-      RFP2_MOE_STAGE(s + 1, sm[1], sm[0], wb0, wb1)
-    }
-#undef TWO
+    RFP2_MOE_LOOP(true)
   } else {
-#define TWO false
-    for (int s = 0; s < nst; s += 2) {
-      RFP2_MOE_STAGE(s, sm[0], sm[1], wa0, wa1)
-      RFP2_MOE_STAGE(s + 1, sm[1], sm[0], wb0, wb1)
-    }
-#undef TWO
+    RFP2_MOE_LOOP(false)
   }
-#undef RFP2_MOE_STAGE
+#undef RFP2_MOE_LOOP
 #undef RFP2_MOE_STEP
 
   // lane -> token, register r -> row; rows n..n+3 of a register group are
