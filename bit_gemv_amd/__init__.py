@@ -52,7 +52,7 @@ _SIGNATURES = {
     "rfp2_debug_half_dots": ([_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
     "rfp2_debug_half_sums_mf": ([_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p], ctypes.c_int),
     "rfp2_debug_decode_f16": ([_c_p, _c_i64, _c_i64, ctypes.c_int, _c_p, _c_p], ctypes.c_int),
-    "rfp2_debug_decode_i8": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p], ctypes.c_int),
+    "rfp2_debug_decode_i8": ([_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p], ctypes.c_int),
 }
 
 
@@ -314,9 +314,11 @@ def rfp2_debug_decode_f16(w, N: int, K: int, form: int, h_out, stream=None) -> N
         _ptr(h_out, torch.int16, N * K, "h_out"), _stream(stream)))
 
 
-def rfp2_debug_decode_i8(w, N: int, K: int, codes_out, scales_out, stream=None) -> None:
+def rfp2_debug_decode_i8(w, N: int, K: int, wa_out, wb_out, scales_out, stream=None) -> None:
+    """wa_out, wb_out: int8 [N, K]; scales_out: fp32 [N, K/32, 6]."""
     import torch
     _check("rfp2_debug_decode_i8", lib().rfp2_debug_decode_i8(
         _ptr(w, torch.uint8, N * _blocks(K) * 10, "w"), N, K,
-        _ptr(codes_out, torch.int8, N * K, "codes_out"),
-        _ptr(scales_out, torch.float32, N * K // 16, "scales_out"), _stream(stream)))
+        _ptr(wa_out, torch.int8, N * K, "wa_out"),
+        _ptr(wb_out, torch.int8, N * K, "wb_out"),
+        _ptr(scales_out, torch.float32, N * _blocks(K) * 6, "scales_out"), _stream(stream)))

@@ -2,40 +2,54 @@
 //
 // Method ("ROCmFP2 codebook research report", "03 · Runtime", applied to a
 // tile of activation columns): the stored blocks are expanded to int8 once
-// per tile and reused by every token of the tile; each 16-weight half gives
-// an int32 partial per (token, row); the two weight scales and the token's
-// activation scale are applied to the partials,
-//   y[m,n] += d[m,b] * (s0[n,b] * P0[m,n] + s1[n,b] * P1[m,n]).
+// per tile and reused by every token of the tile; the integer dot products
+// are rescaled by the weight scales and the token's activation scale,
+//   y[m,n] += d[m,b] * (s0[n,b] * P0[m,n] + s1[n,b] * P1[m,n]),
+// P_h the int32 sum over half h of block b.
+//
+// Folded operands.  A legal UE4M3 scale byte is s = mu * 2^(x - 11) with x =
+// max(E, 1) and mu = 8 + M (mu = M when E = 0), at most 4 bits.  For a block
+// with x_lo = min(x0, x1),
+//   s0 * P0 + s1 * P1 = 2^(x_lo - 11) * sum_k a_k * (level_k * c_h),
+//   c_h = mu_h * 2^(x_h - x_lo),
+// an integer dot product with one power-of-two scale.  When the halves'
+// exponents differ by at most 2, |level * c| <= 4 * 60 = 240: one
+// v_mfma_i32_16x16x64_i8 takes it whole, its 64 k being the block's 32
+// activations twice against two int8 operands wA + wB (a weight whose c is
+// 32..60 is split into two equal parts).  That replaces the two per-half
+// partials and the per-half scales of the direct form.
+//   Blocks whose exponents differ by 3 or more (0.4 % of the blocks of the
+// synthetic weights) keep their halves apart: wA = the half of larger
+// exponent (level * mu), wB = the other one, each with its own power-of-two
+// scale.  A 16-row tile holding such a block in a stage takes the split
+// path: one more MFMA (wA alone) and three more instructions per output.
+//
+// Rescale: the int32 sum accumulates onto the bits of 1.5 * 2^23, so read as
+// fp32 it is 1.5 * 2^23 + P exactly (|P| <= 32 * 127 * 240 < 2^22), and
+// fma(x, s, -1.5 * 2^23 * s) = s * P exactly (s a power of two); then
+// fma(d, ., acc).  Two instructions per (token, row, block): the vector ALU
+// work that bounds this kernel (the matrix cores are far from busy).
 //
 // gfx950 mapping
-//   * v_mfma_i32_32x32x16_i8: one instruction is exactly one 16-weight half
-//     (K = 16) of a 32 x 32 (token x row) tile, so every int32 partial is a
-//     per-half sum and no weight scale is mixed into another.
-//   * Workgroup tile 128 tokens x 128 rows, four waves of 64 x 64 (2 x 2
-//     MFMA tiles); K advances 128 weights (4 blocks) per LDS stage.  Two LDS
-//     buffers: while the waves compute stage s, the global loads of stage s+1
-//     are already in registers; one barrier per stage.  Two workgroups per
-//     CU.
-//   * Weights are expanded in registers (expand_half) and written to LDS as
-//     int8 in the lane order of expand_half; activations are staged with the
-//     same within-half permutation (transpose_half), so the dot product over
-//     each half is unchanged.  Row strides of 136 bytes keep the 8-byte LDS
-//     operand reads of 32 lanes on distinct banks.
-//   * The fp32 rescale of every (token, row, block) is vector-ALU work that
-//     no MFMA shape removes: per-half weight scales and per-block activation
-//     scales both vary along K.  It, not the matrix cores, bounds this
-//     kernel.  Four instructions instead of five: the first half's partial
-//     is accumulated onto the int32 bit pattern of 1.5 * 2^23, so the result
-//     read as fp32 is exactly 1.5 * 2^23 + P0 (|P0| <= 16 * 4 * 127 < 2^22),
-//     and s0 * P0 = fma(s0, that, -1.5 * 2^23 * s0) in one instruction,
-//     exact (s0 has at most 4 significant bits, s0 * P0 at most 17) -- the
-//     same value as the convert and multiply it replaces, so the outputs
-//     are unchanged; then one convert of P1, fma(s1, P1, s0 * P0), and the
-//     fma with the activation scale.
+//   * Workgroup tile 112 rows x 256 tokens, eight waves (two per SIMD), one
+//     workgroup per CU; wave w owns tokens 32w..32w+31 (two 16-token MFMA
+//     tiles) and all seven 16-row tiles, so the decoded weights in LDS serve
+//     all eight waves.  (For 512 x 14336 this is 2 x 128 = 256 workgroups.)
+//   * MFMA operand A = activations (i = token), B = weights (j = row): lane
+//     l holds row l % 16 of each tile and tokens 4 (l / 16) + r in its
+//     registers r, so the row scales are one register per tile and the
+//     activation scales one 16-byte LDS read per token tile.
+//   * Stages of 2 blocks in two LDS buffers; the global loads of stage s + 2
+//     are in flight while stage s is computed and stage s + 1 is staged; one
+//     barrier per stage.
+//   * Weights are expanded in registers (the per-half level table scaled by
+//     the multiplier, looked up by byte permutes) into the lane order of
+//     expand_half; activations are staged with the same within-half
+//     permutation (transpose_half), so each dot product is unchanged.
 //   * Workgroup -> tile order is XCD-aware: the hardware deals workgroups to
-//     the 8 XCDs round-robin, so consecutive tiles are given to workgroups
-//     that land on the same XCD, and the token tiles of one row tile run
-//     next to each other and share that XCD's L2 for the weights.
+//     the 8 XCDs round-robin, so consecutive tiles (the token tiles of one
+//     row tile first) are given to workgroups on the same XCD and share its
+//     L2 for the weights.
 #include "rfp2_device.h"
 #include "rfp2_internal.h"
 
@@ -43,247 +57,360 @@ namespace rfp2 {
 
 namespace {
 
-typedef int v16i __attribute__((ext_vector_type(16)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef short v2s __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128;          // tokens per workgroup tile
-constexpr int BN = 128;          // weight rows per workgroup tile
-constexpr int BKB = 4;           // blocks (of 32 weights) per LDS stage
-constexpr int kStride = BKB * 32 + 8;   // LDS bytes per row of a stage (136)
+constexpr int kRowTiles = 7;                // 16-row MFMA tiles per workgroup
+constexpr int BN = 16 * kRowTiles;          // 112 weight rows per workgroup
+constexpr int kWaves = 8;
+constexpr int BM = 32 * kWaves;             // 256 tokens per workgroup
+constexpr int KB = 2;                       // blocks per LDS stage
+constexpr int kWRow = KB * 64 + 16;         // LDS bytes per weight row of a stage (144)
+constexpr int kARow = KB * 32 + 16;         // LDS bytes per token row of a stage (80)
+constexpr int kDecoders = 56;               // decoding lanes in each of waves 0..3
 constexpr int kXcds = 8;
+constexpr int kBiasBits = 0x4B400000;       // fp32 1.5 * 2^23
+constexpr float kNegBias = -12582912.0f;
+
+// The staged form of one block of one row.
+struct Folded {
+  uint32_t wa[2][4], wb[2][4];  // [half][word], expand_half lane order
+  float2 sm;                    // (s, -1.5*2^23*s); s < 0 (or NaN): split path
+  float4 sg;                    // (sA, -1.5*2^23*sA, sB, -1.5*2^23*sB)
+};
+
+// Bytes [-4c, -c, c, 4c] (code 0..3 -> level * c), 0 <= c <= 31.
+__device__ __forceinline__ uint32_t level_table(uint32_t c) {
+  const uint32_t pos = c * 0x10004u;        // 16-bit lanes (4c, c)
+  const v2s n = v2s{0, 0} - __builtin_bit_cast(v2s, pos);
+  return __builtin_amdgcn_perm(pos, __builtin_bit_cast(uint32_t, n), 0x04060200u);
+}
+
+__device__ __forceinline__ float pow2_scale(int x) {    // 2^(x - 11), 1 <= x <= 31
+  return __int_as_float((x + 116) << 23);
+}
+
+// Fold one block: C0, C1 the two halves' code words, sc = e0 | e1 << 8.
+__device__ __forceinline__ void fold_block(uint32_t C0, uint32_t C1, uint32_t sc,
+                                           Folded& f) {
+  const int e0 = sc & 0xFF, e1 = (sc >> 8) & 0xFF;
+  const int x0 = max(e0 >> 3, 1), x1 = max(e1 >> 3, 1);
+  const int mu0 = e0 + 8 - 8 * x0, mu1 = e1 + 8 - 8 * x1;
+  const int xl = min(x0, x1), xh = max(x0, x1);
+  const bool near = xh - xl <= 2;
+  const int c0 = near ? mu0 << (x0 - xl) : mu0;
+  const int c1 = near ? mu1 << (x1 - xl) : mu1;
+  // near: c > 31 only for c = 4 mu (exponent step 2), split into two 2 mu
+  const int h0 = c0 > 31 ? c0 >> 1 : c0, h1 = c1 > 31 ? c1 >> 1 : c1;
+  const bool top0 = x0 > x1;                // apart: half 0 has the larger exponent
+  const int a0 = near ? h0 : (top0 ? c0 : 0), b0 = near ? c0 - h0 : (top0 ? 0 : c0);
+  const int a1 = near ? h1 : (top0 ? 0 : c1), b1 = near ? c1 - h1 : (top0 ? c1 : 0);
+  const uint32_t tA0 = level_table(a0), tB0 = level_table(b0);
+  const uint32_t tA1 = level_table(a1), tB1 = level_table(b1);
+  // selectors: byte j of word i = code of weight 4j + i (as expand_block)
+  const uint64_t C = ((uint64_t)C1 << 32) | C0;
+  const uint64_t S2 = shr64<2>(C), S4 = shr64<4>(C), S6 = shr64<6>(C);
+  const uint32_t sel[2][4] = {
+      {C0 & kLow2, (uint32_t)S2 & kLow2, (uint32_t)S4 & kLow2, (uint32_t)S6 & kLow2},
+      {C1 & kLow2, (uint32_t)(S2 >> 32) & kLow2, (uint32_t)(S4 >> 32) & kLow2,
+       (uint32_t)(S6 >> 32) & kLow2}};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.wa[0][i] = __builtin_amdgcn_perm(tA0, tA0, sel[0][i]);
+    f.wb[0][i] = __builtin_amdgcn_perm(tB0, tB0, sel[0][i]);
+    f.wa[1][i] = __builtin_amdgcn_perm(tA1, tA1, sel[1][i]);
+    f.wb[1][i] = __builtin_amdgcn_perm(tB1, tB1, sel[1][i]);
+  }
+  const bool bad = scale_byte_bad(e0) || scale_byte_bad(e1);
+  const float nan = __builtin_nanf("");
+  const float sl = bad ? nan : pow2_scale(xl);
+  const float sa = bad ? nan : (near ? sl : pow2_scale(xh));
+  f.sg = make_float4(sa, kNegBias * sa, sl, kNegBias * sl);
+  f.sm = make_float2(near ? sl : -sl, kNegBias * sl);
+}
+
+// Block `blk` (0 or 1) of a dword-aligned 20-byte pair of blocks.
+__device__ __forceinline__ void fold_pair_member(const uint32_t (&wd)[5], int blk, Folded& f) {
+  const uint32_t C0 = blk ? __builtin_amdgcn_alignbit(wd[3], wd[2], 16) : wd[0];
+  const uint32_t C1 = blk ? __builtin_amdgcn_alignbit(wd[4], wd[3], 16) : wd[1];
+  const uint32_t sc = blk ? wd[4] >> 16 : wd[2] & 0xFFFFu;
+  fold_block(C0, C1, sc, f);
+}
 
 struct __align__(16) Stage {
-  int8_t wq[BN * kStride];       // expanded weights, permuted within halves
-  int8_t aq[BM * kStride];       // activations, same permutation
-  float ws[BN][BKB * 2];         // weight scale per (row, half)
-  float ad[BKB][BM];             // activation scale per (block, token)
+  uint8_t w[BN * kWRow];        // row r, block b: [wA h0 | wA h1 | wB h0 | wB h1]
+  uint8_t a[BM * kARow];        // token t, block b: [h0 | h1], transposed halves
+  float2 sm[KB][BN];
+  float4 sg[KB][BN];
+  float d[KB][BM];
 };
 
 struct Prefetch {
-  uint32_t wd[5];                // two blocks of one weight row
-  uint4 a[4];                    // 64 bytes of one token's activations
-  float d[2];                    // two activation scales
+  uint32_t wd[5];               // the decoded row's 20-byte pair (decoding lanes)
+  uint4 a0, a1;                 // one block of one token's activations
+  float d;
 };
 
-__device__ __forceinline__ void fetch(Prefetch& f, const uint8_t* __restrict__ w,
-                                      const int8_t* __restrict__ q,
-                                      const float* __restrict__ d, int64_t row_bytes,
-                                      int K, int nb, int kb, int tid, int n0, int m0,
-                                      int N, int M) {
-  const int wrow = tid >> 1, wpair = tid & 1;
-  // rows / tokens past the end read row / token 0 (never stored)
-  const int n = n0 + wrow < N ? n0 + wrow : 0;
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(
-      w + (int64_t)n * row_bytes + (int64_t)(kb + 2 * wpair) * 10);
+struct Roles {
+  bool dec;                     // this lane decodes (row drow, block dblk)
+  int drow, dblk;
+  const uint8_t* w;             // decoded row
+  int atok, ablk;               // staged (token, block)
+  const int8_t* q;
+  const float* d;
+};
+
+__device__ __forceinline__ void fetch(Prefetch& f, const Roles& r, int kb) {
+  if (r.dec) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(r.w + (int64_t)kb * 10);
 #pragma unroll
-  for (int i = 0; i < 5; ++i) f.wd[i] = src[i];
-  const int arow = tid >> 1, ahalf = tid & 1;
-  const int m = m0 + arow < M ? m0 + arow : 0;
-  const uint4* asrc = reinterpret_cast<const uint4*>(q + (int64_t)m * K + (int64_t)kb * 32 +
-                                                     ahalf * 64);
+    for (int i = 0; i < 5; ++i) f.wd[i] = src[i];
+  }
+  const uint4* asrc = reinterpret_cast<const uint4*>(r.q + (int64_t)kb * 32);
+  f.a0 = asrc[0];
+  f.a1 = asrc[1];
+  f.d = r.d[kb];
+}
+
+__device__ __forceinline__ void stage_to_lds(const Prefetch& f, Stage& st, const Roles& r) {
+  if (r.dec) {
+    Folded fb;
+    fold_pair_member(f.wd, r.dblk, fb);
+    uint4* dst = reinterpret_cast<uint4*>(st.w + r.drow * kWRow + r.dblk * 64);
+    dst[0] = make_uint4(fb.wa[0][0], fb.wa[0][1], fb.wa[0][2], fb.wa[0][3]);
+    dst[1] = make_uint4(fb.wa[1][0], fb.wa[1][1], fb.wa[1][2], fb.wa[1][3]);
+    dst[2] = make_uint4(fb.wb[0][0], fb.wb[0][1], fb.wb[0][2], fb.wb[0][3]);
+    dst[3] = make_uint4(fb.wb[1][0], fb.wb[1][1], fb.wb[1][2], fb.wb[1][3]);
+    st.sm[r.dblk][r.drow] = fb.sm;
+    st.sg[r.dblk][r.drow] = fb.sg;
+  }
+  uint32_t A0[4], A1[4];
+  {
+    const uint32_t X0[4] = {f.a0.x, f.a0.y, f.a0.z, f.a0.w};
+    const uint32_t X1[4] = {f.a1.x, f.a1.y, f.a1.z, f.a1.w};
+    transpose_half(X0, A0);
+    transpose_half(X1, A1);
+  }
+  uint4* adst = reinterpret_cast<uint4*>(st.a + r.atok * kARow + r.ablk * 32);
+  adst[0] = make_uint4(A0[0], A0[1], A0[2], A0[3]);
+  adst[1] = make_uint4(A1[0], A1[1], A1[2], A1[3]);
+  st.d[r.ablk][r.atok] = f.d;
+}
+
+// y += d * u for one row tile, u the tile's block sums times their scales.
+__device__ __forceinline__ void accumulate(const v4f (&dv)[2], const float (&u)[2][4],
+                                           v4f (&acc)[2]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = asrc[i];
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid * 2 + i;        // 512 = BKB * BM scales
-    const int blk = idx / BM, mm = idx % BM;
-    const int mr = m0 + mm < M ? m0 + mm : 0;
-    f.d[i] = d[(int64_t)mr * nb + kb + blk];
+    for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(dv[t][r], u[t][r], acc[t][r]);
+}
+
+// Folded form: P = 1.5*2^23 + the block's sum, u = s * sum (exact).
+__device__ __forceinline__ void folded_sums(const v4i (&P)[2], float2 s, float (&u)[2][4]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) u[t][r] = fmaf(__int_as_float(P[t][r]), s.x, s.y);
+}
+
+// Split form for a tile with a block whose halves stay apart (or an illegal
+// scale byte: NaN): wA's part recomputed alone, u = sA * PA + sB * PB.
+__device__ __forceinline__ void split_sums(const Stage& st, int blk, int rt, int g, int li,
+                                           const v4i& bias, const v4i (&a)[2],
+                                           const v4i (&P)[2], float (&u)[2][4]) {
+  const float4 sg = st.sg[blk][16 * rt + li];
+  const v4i b = *reinterpret_cast<const v4i*>(st.w + (16 * rt + li) * kWRow + blk * 64 + 16 * g);
+  const v4i bA = g < 2 ? b : v4i{0, 0, 0, 0};     // lane groups 2, 3 hold wB
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const v4i PA = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], bA, bias, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      u[t][r] = fmaf((float)(P[t][r] - PA[r]), sg.z, fmaf(__int_as_float(PA[r]), sg.x, sg.y));
   }
 }
 
-__device__ __forceinline__ void stage_to_lds(const Prefetch& f, Stage& st, int tid) {
-  const int wrow = tid >> 1, wpair = tid & 1;
-  const uint32_t codes[4] = {f.wd[0], f.wd[1], __builtin_amdgcn_alignbit(f.wd[3], f.wd[2], 16),
-                             __builtin_amdgcn_alignbit(f.wd[4], f.wd[3], 16)};
+// The stage's block sums for this wave's 112 rows x 32 tokens, rescaled and
+// added to acc[row tile][token tile].  A block's LDS operands are all read
+// first (one wait per block instead of one per tile), then the tiles are
+// software-pipelined (the MFMAs of tile rt + 1 are issued before tile rt is
+// rescaled).  Every tile takes the folded form first; a tile that needs the
+// split form (s <= 0 or NaN on one of its rows, rare) has its u recomputed
+// in a branch that touches nothing else, so the accumulators never meet a
+// branch (where the compiler would copy them).
+__device__ __forceinline__ void compute_stage(const Stage& st, int wave, int lane,
+                                              const v4i& bias, v4f (&acc)[kRowTiles][2]) {
+  const int g = lane >> 4, li = lane & 15;
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {   // the four halves of the two blocks
-    uint32_t W[4];
-    expand_half(codes[h], W);
-    int8_t* dst = st.wq + wrow * kStride + (2 * wpair) * 32 + h * 16;
-    *reinterpret_cast<uint2*>(dst) = make_uint2(W[0], W[1]);
-    *reinterpret_cast<uint2*>(dst + 8) = make_uint2(W[2], W[3]);
-  }
-  // an illegal scale byte in a block makes both of its scales NaN (bit-or
-  // with a quiet NaN pattern: no branch)
-  const uint32_t nan0 = scale_flags_set<0>(scale_pair_bad<0>(f.wd[2])) ? 0x7FC00000u : 0u;
-  const uint32_t nan1 = scale_flags_set<1>(scale_pair_bad<1>(f.wd[4])) ? 0x7FC00000u : 0u;
-  float4 s;
-  s.x = __uint_as_float(__float_as_uint(fp8_byte<0>(f.wd[2])) | nan0);
-  s.y = __uint_as_float(__float_as_uint(fp8_byte<1>(f.wd[2])) | nan0);
-  s.z = __uint_as_float(__float_as_uint(fp8_byte<2>(f.wd[4])) | nan1);
-  s.w = __uint_as_float(__float_as_uint(fp8_byte<3>(f.wd[4])) | nan1);
-  *reinterpret_cast<float4*>(&st.ws[wrow][4 * wpair]) = s;
-
-  const int arow = tid >> 1, ahalf = tid & 1;
+  for (int blk = 0; blk < KB; ++blk) {
+    v4i a[2], b[kRowTiles];
+    v4f dv[2];
+    float2 s[kRowTiles];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t X[4] = {f.a[i].x, f.a[i].y, f.a[i].z, f.a[i].w};
-    uint32_t A[4];
-    transpose_half(X, A);
-    int8_t* dst = st.aq + arow * kStride + ahalf * 64 + i * 16;
-    *reinterpret_cast<uint2*>(dst) = make_uint2(A[0], A[1]);
-    *reinterpret_cast<uint2*>(dst + 8) = make_uint2(A[2], A[3]);
-  }
+    for (int t = 0; t < 2; ++t) {
+      const int tok = 32 * wave + 16 * t;
+      a[t] = *reinterpret_cast<const v4i*>(st.a + (tok + li) * kARow + blk * 32 + 16 * (g & 1));
+      dv[t] = *reinterpret_cast<const v4f*>(&st.d[blk][tok + 4 * g]);
+    }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid * 2 + i;
-    st.ad[idx / BM][idx % BM] = f.d[i];
+    for (int rt = 0; rt < kRowTiles; ++rt) {
+      b[rt] = *reinterpret_cast<const v4i*>(st.w + (16 * rt + li) * kWRow + blk * 64 + 16 * g);
+      s[rt] = st.sm[blk][16 * rt + li];
+    }
+    v4i P[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) P[0][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], b[0], bias, 0, 0, 0);
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt) {
+      if (rt + 1 < kRowTiles) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          P[(rt + 1) & 1][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], b[rt + 1], bias, 0, 0, 0);
+      }
+      float u[2][4];
+      folded_sums(P[rt & 1], s[rt], u);
+      if (__builtin_expect(__ballot(!(s[rt].x > 0.0f)) != 0, 0))
+        split_sums(st, blk, rt, g, li, bias, a, P[rt & 1], u);
+      accumulate(dv, u, acc[rt]);
+      // keep the update here: sunk to the end of the block, the seven
+      // tiles' u would all be live at once
+      asm volatile("" : "+v"(acc[rt][0]), "+v"(acc[rt][1]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-__global__ __launch_bounds__(256, 2) void gemm_kernel(
+__global__ __launch_bounds__(512) void gemm_kernel(
     const uint8_t* __restrict__ w, int N, int K, const int8_t* __restrict__ q,
-    const float* __restrict__ d, int M, float* __restrict__ y, int m_tiles,
-    int tiles) {
+    const float* __restrict__ d, int M, float* __restrict__ y, int m_tiles, int tiles) {
   __shared__ Stage sm[2];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-  // XCD-aware order: workgroup b runs on XCD b % 8; give XCD x the
-  // consecutive tiles x*per, x*per+1, ... (token tiles of a row tile first)
   int tile = blockIdx.x;
   if (tiles % kXcds == 0) tile = (blockIdx.x % kXcds) * (tiles / kXcds) + blockIdx.x / kXcds;
-  const int mt = tile % m_tiles;
-  const int nt = tile / m_tiles;
-  const int m0 = mt * BM, n0 = nt * BN;
-  const int64_t row_bytes = (int64_t)(K / 32) * 10;
+  const int m0 = (tile % m_tiles) * BM;
+  const int n0 = (tile / m_tiles) * BN;
   const int nb = K / 32;
-  const int stages = nb / BKB;
+  const int64_t row_bytes = (int64_t)nb * 10;
+  const int stages = nb / KB;
 
-  float facc[2][2][16];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) facc[i][j][r] = 0.0f;
-
-  // the accumulator start of the first half's partials: fp32 1.5 * 2^23
-  v16i kBias;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) kBias[r] = 0x4B400000;
-  Prefetch f;
-  fetch(f, w, q, d, row_bytes, K, nb, 0, tid, n0, m0, N, M);
-  const int koff_lane = 8 * (lane >> 5);
-  for (int s = 0; s < stages; ++s) {
-    Stage& st = sm[s & 1];
-    stage_to_lds(f, st, tid);
-    if (s + 1 < stages) fetch(f, w, q, d, row_bytes, K, nb, (s + 1) * BKB, tid, n0, m0, N, M);
-    __syncthreads();
-
-#pragma unroll
-    for (int blk = 0; blk < BKB; ++blk) {
-      long a[2][2];                 // [half][tm]
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int tm = 0; tm < 2; ++tm)
-          a[h][tm] = *reinterpret_cast<const long*>(
-              st.aq + (wm * 64 + tm * 32 + (lane & 31)) * kStride + blk * 32 + h * 16 +
-              koff_lane);
-#pragma unroll
-      for (int tn = 0; tn < 2; ++tn) {
-        const int n = wn * 64 + tn * 32 + (lane & 31);
-        const long b0 = *reinterpret_cast<const long*>(st.wq + n * kStride + blk * 32 + koff_lane);
-        const long b1 =
-            *reinterpret_cast<const long*>(st.wq + n * kStride + blk * 32 + 16 + koff_lane);
-        const float2 sc = *reinterpret_cast<const float2*>(&st.ws[n][2 * blk]);
-        const float nb0 = -12582912.0f * sc.x;
-#pragma unroll
-        for (int tm = 0; tm < 2; ++tm) {
-          const v16i P0 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a[0][tm], b0, kBias, 0, 0, 0);
-          const v16i P1 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a[1][tm], b1, v16i{}, 0, 0, 0);
-          // lane holds row n of the tile and tokens
-          // (r % 4) + 8 * (r / 4) + 4 * (lane / 32), r = 0..15
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const float4 dv = *reinterpret_cast<const float4*>(
-                &st.ad[blk][wm * 64 + tm * 32 + 8 * p + 4 * (lane >> 5)]);
-            const float dd[4] = {dv.x, dv.y, dv.z, dv.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * p + e;
-              const float t = fmaf(sc.y, (float)P1[r], fmaf(sc.x, __int_as_float(P0[r]), nb0));
-              facc[tm][tn][r] = fmaf(dd[e], t, facc[tm][tn][r]);
-            }
-          }
-        }
-      }
-    }
+  // rows / tokens past the end read row N-1 / token M-1 (never stored)
+  Roles ro;
+  {
+    // two consecutive lanes take the two blocks of one row / token (their
+    // global loads then cover whole 20- and 64-byte pieces; mapping
+    // consecutive lanes to consecutive rows and tokens removed a quarter of
+    // the LDS bank conflicts of the stores but cost 2 and 8 us)
+    const int di = kDecoders * wave + lane;
+    ro.dec = wave < 4 && lane < kDecoders;
+    ro.drow = di >> 1;
+    ro.dblk = di & 1;
+    ro.w = w + (int64_t)min(n0 + ro.drow, N - 1) * row_bytes;
+    ro.atok = tid >> 1;
+    ro.ablk = tid & 1;
+    const int64_t tok = min(m0 + ro.atok, M - 1);
+    ro.q = q + tok * K + ro.ablk * 32;
+    ro.d = d + tok * nb + ro.ablk;
   }
 
-  const float fix = scale_fix();
+  v4f acc[kRowTiles][2];
 #pragma unroll
-  for (int tm = 0; tm < 2; ++tm)
+  for (int i = 0; i < kRowTiles; ++i)
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn) {
-      const int n = n0 + wn * 64 + tn * 32 + (lane & 31);
-      if (n >= N) continue;
+    for (int t = 0; t < 2; ++t) acc[i][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // the MFMA accumulator start, held in registers (as a constant the
+  // compiler rebuilds it from scalar registers before every MFMA)
+  v4i bias = {kBiasBits, kBiasBits, kBiasBits, kBiasBits};
+  asm volatile("" : "+v"(bias));
+
+  Prefetch f;
+  fetch(f, ro, 0);
+  stage_to_lds(f, sm[0], ro);
+  fetch(f, ro, stages > 1 ? KB : 0);
+  __syncthreads();
+  for (int s = 0; s + 1 < stages; ++s) {
+    compute_stage(sm[s & 1], wave, lane, bias, acc);
+    stage_to_lds(f, sm[(s + 1) & 1], ro);
+    fetch(f, ro, (s + 2 < stages ? s + 2 : stages - 1) * KB);
+    __syncthreads();
+  }
+  compute_stage(sm[(stages - 1) & 1], wave, lane, bias, acc);
+
+  const int g = lane >> 4, li = lane & 15;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + tm * 32 + (r & 3) + 8 * (r >> 2) + 4 * (lane >> 5);
-        if (m < M) y[(int64_t)m * N + n] = facc[tm][tn][r] * fix;
+  for (int rt = 0; rt < kRowTiles; ++rt) {
+    const int n = n0 + 16 * rt + li;
+    if (n >= N) continue;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 32 * wave + 16 * t + 4 * g + r;
+        if (m < M) y[(int64_t)m * N + n] = acc[rt][t][r];
       }
-    }
+  }
 }
 
-// Inspection of the GEMM's decode (rfp2_debug_decode_i8): the two blocks of
-// pair p of the flat block stream, loaded and decoded exactly as
-// stage_to_lds decodes a thread's pair (the second block funnel-shifted out
-// of the dwords), written in natural weight order.
+// Inspection of the GEMM's decode (rfp2_debug_decode_i8): block 2p + j of
+// the flat block stream is folded from its 20-byte pair exactly as a
+// staging lane folds member j of the pair it loaded, and written out in
+// natural weight order with its scales.
 __global__ __launch_bounds__(256) void debug_decode_i8_kernel(
-    const uint8_t* __restrict__ w, int64_t nblocks, uint32_t* __restrict__ codes,
-    float* __restrict__ scales) {
-  const float fix = scale_fix();
-  for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < (nblocks + 1) / 2;
-       p += (int64_t)gridDim.x * 256) {
+    const uint8_t* __restrict__ w, int64_t nblocks, int8_t* __restrict__ wa_out,
+    int8_t* __restrict__ wb_out, float* __restrict__ s_out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nblocks;
+       i += (int64_t)gridDim.x * 256) {
     // the 20-byte pair as 16-bit pieces (the stream is only 2-byte aligned
     // here); bytes past the end read as zero
+    const int64_t p = i >> 1;
     const uint16_t* src = reinterpret_cast<const uint16_t*>(w + p * 20);
     const int64_t end = nblocks * 10;
-    Prefetch f;
+    uint32_t wd[5];
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const int64_t off = p * 20 + 4 * i;
-      f.wd[i] = (off < end ? (uint32_t)src[2 * i] : 0u) |
-                ((off + 2 < end ? (uint32_t)src[2 * i + 1] : 0u) << 16);
+    for (int k = 0; k < 5; ++k) {
+      const int64_t off = p * 20 + 4 * k;
+      wd[k] = (off < end ? (uint32_t)src[2 * k] : 0u) |
+              ((off + 2 < end ? (uint32_t)src[2 * k + 1] : 0u) << 16);
     }
-    const uint32_t cw[4] = {f.wd[0], f.wd[1], __builtin_amdgcn_alignbit(f.wd[3], f.wd[2], 16),
-                            __builtin_amdgcn_alignbit(f.wd[4], f.wd[3], 16)};
-    const float nan = __builtin_nanf("");
-    const bool bad0 = scale_flags_set<0>(scale_pair_bad<0>(f.wd[2]));
-    const bool bad1 = scale_flags_set<1>(scale_pair_bad<1>(f.wd[4]));
-    const float sv[4] = {bad0 ? nan : fp8_byte<0>(f.wd[2]) * fix,
-                         bad0 ? nan : fp8_byte<1>(f.wd[2]) * fix,
-                         bad1 ? nan : fp8_byte<2>(f.wd[4]) * fix,
-                         bad1 ? nan : fp8_byte<3>(f.wd[4]) * fix};
+    Folded f;
+    fold_pair_member(wd, (int)(i & 1), f);
+    // weight 4j + c of a half is byte j of word c
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {              // the four halves of the pair
-      const int64_t blk = 2 * p + (h >> 1);
-      if (blk >= nblocks) break;
-      uint32_t W[4];
-      expand_half(cw[h], W);
-      // weight 4j+i of the half is byte j of W[i]
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = __builtin_amdgcn_perm(W[1], W[0], 0x00000400u + 0x0101u * j);
-        const uint32_t hi = __builtin_amdgcn_perm(W[3], W[2], 0x00000400u + 0x0101u * j);
-        codes[blk * 8 + (h & 1) * 4 + j] = (lo & 0xFFFFu) | (hi << 16);
+        const uint32_t sel = 0x0C0C0C00u + (uint32_t)j;   // byte j of each word to byte 0
+        uint32_t va = 0, vb = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          va |= (__builtin_amdgcn_perm(0u, f.wa[h][c], sel) & 0xFFu) << (8 * c);
+          vb |= (__builtin_amdgcn_perm(0u, f.wb[h][c], sel) & 0xFFu) << (8 * c);
+        }
+        *reinterpret_cast<uint32_t*>(wa_out + i * 32 + 16 * h + 4 * j) = va;
+        *reinterpret_cast<uint32_t*>(wb_out + i * 32 + 16 * h + 4 * j) = vb;
       }
-      scales[blk * 2 + (h & 1)] = sv[h];
-    }
+    float* so = s_out + i * 6;
+    so[0] = f.sm.x;
+    so[1] = f.sm.y;
+    so[2] = f.sg.x;
+    so[3] = f.sg.y;
+    so[4] = f.sg.z;
+    so[5] = f.sg.w;
   }
 }
 
 }  // namespace
 
-hipError_t launch_debug_decode_i8(const uint8_t* w, int64_t N, int64_t K, int8_t* codes,
-                                  float* scales, hipStream_t stream) {
-  const int64_t npairs = (N * (K / 32) + 1) / 2;
-  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((npairs + 255) / 256, kMaxGrid));
+hipError_t launch_debug_decode_i8(const uint8_t* w, int64_t N, int64_t K, int8_t* wa,
+                                  int8_t* wb, float* scales, hipStream_t stream) {
+  const int64_t nblocks = N * (K / 32);
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((nblocks + 255) / 256, kMaxGrid));
   hipLaunchKernelGGL(debug_decode_i8_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, w,
-                     N * (K / 32), reinterpret_cast<uint32_t*>(codes), scales);
+                     nblocks, wa, wb, scales);
   return hipGetLastError();
 }
 
@@ -292,7 +419,7 @@ hipError_t launch_gemm(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
   const int m_tiles = (int)((M + BM - 1) / BM);
   const int n_tiles = (int)((N + BN - 1) / BN);
   const int tiles = m_tiles * n_tiles;
-  hipLaunchKernelGGL(gemm_kernel, dim3((uint32_t)tiles), dim3(256), 0, stream, w, (int)N,
+  hipLaunchKernelGGL(gemm_kernel, dim3((uint32_t)tiles), dim3(512), 0, stream, w, (int)N,
                      (int)K, q, d, (int)M, y, m_tiles, tiles);
   return hipGetLastError();
 }

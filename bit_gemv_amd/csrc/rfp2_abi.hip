@@ -284,14 +284,15 @@ rfp2_status rfp2_debug_decode_f16(const uint8_t* w, int64_t N, int64_t K, int fo
   return from_hip(rfp2::launch_debug_decode_f16(w, N, K, form, h_out, stream));
 }
 
-rfp2_status rfp2_debug_decode_i8(const uint8_t* w, int64_t N, int64_t K, int8_t* codes_out,
-                                 float* scales_out, hipStream_t stream) {
-  if (!w || !codes_out || !scales_out) return RFP2_E_NULL;
+rfp2_status rfp2_debug_decode_i8(const uint8_t* w, int64_t N, int64_t K, int8_t* wa_out,
+                                 int8_t* wb_out, float* scales_out, hipStream_t stream) {
+  if (!w || !wa_out || !wb_out || !scales_out) return RFP2_E_NULL;
   if (N < 1 || N > kMaxRows || K < 32 || K % 32 != 0 || K > (int64_t(1) << 30))
     return RFP2_E_SHAPE;
-  if (!aligned(w, 2) || !aligned(codes_out, 4) || !aligned(scales_out, 4)) return RFP2_E_ALIGN;
+  if (!aligned(w, 2) || !aligned(wa_out, 4) || !aligned(wb_out, 4) || !aligned(scales_out, 4))
+    return RFP2_E_ALIGN;
   (void)hipGetLastError();
-  return from_hip(rfp2::launch_debug_decode_i8(w, N, K, codes_out, scales_out, stream));
+  return from_hip(rfp2::launch_debug_decode_i8(w, N, K, wa_out, wb_out, scales_out, stream));
 }
 
 }  // extern "C"

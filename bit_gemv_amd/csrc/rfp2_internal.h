@@ -67,8 +67,8 @@ hipError_t launch_debug_half_dots(const uint8_t* w, int64_t N, int64_t K,
 hipError_t launch_debug_half_sums_mf(const uint8_t* w, int64_t N, int64_t K,
                                      const int8_t* q, int64_t M, int32_t* sums,
                                      hipStream_t stream);
-hipError_t launch_debug_decode_i8(const uint8_t* w, int64_t N, int64_t K, int8_t* codes,
-                                  float* scales, hipStream_t stream);
+hipError_t launch_debug_decode_i8(const uint8_t* w, int64_t N, int64_t K, int8_t* wa,
+                                  int8_t* wb, float* scales, hipStream_t stream);
 hipError_t launch_debug_decode_f16(const uint8_t* w, int64_t N, int64_t K, int form,
                                    uint16_t* out, hipStream_t stream);
 

@@ -128,7 +128,12 @@ rfp2_status rfp2_gemv(const uint8_t* w, int64_t N, int64_t K,
 /*
  * rfp2_gemm -- the same product for a batch of M >= 1 activation columns
  * (prompt batches), computed with i8 matrix-core instructions on int32
- * per-half partials ("03 · Runtime" applied to a tile of columns).
+ * integer sums ("03 · Runtime" applied to a tile of columns).  The UE4M3
+ * mantissas of a block's two scales are folded into its int8 weights, so
+ * the block is one integer dot product with one power-of-two scale while
+ * the two scale exponents differ by at most 2 (as int32 per-half partials
+ * otherwise); every such scaled sum is exact and the activation scale is
+ * applied to it with one rounding, then added with one more.
  * Layouts and alignment as rfp2_gemv.  Requires N >= 1, M >= 1,
  * 256 <= K <= 2^24, K % 256 == 0.
  */
@@ -144,7 +149,7 @@ rfp2_status rfp2_gemm(const uint8_t* w, int64_t N, int64_t K,
  * core in fp32 (exact while the two scale exponents differ by at most 7;
  * beyond, the core's fp32 accumulation may round, each step within 2^-24 of
  * the running sum) and only the activation scale is applied afterwards: one
- * multiply-add per output and block instead of the int32 path's five.
+ * multiply-add per output and block instead of the int32 path's two.
  * Layouts, alignment and limits as rfp2_gemm.
  */
 rfp2_status rfp2_gemm_f16(const uint8_t* w, int64_t N, int64_t K,
@@ -369,16 +374,20 @@ rfp2_status rfp2_debug_decode_f16(const uint8_t* w, int64_t N, int64_t K, int fo
 
 /*
  * rfp2_debug_decode_i8: the decode of rfp2_gemm (the int8 matrix-core
- * product): blocks taken in dword-aligned 20-byte pairs, as a GEMM thread
- * loads them (the second block of a pair starts at byte 2 of a dword), each
- * half expanded to its int8 lanes and its scale converted as the GEMM stages
- * them.  codes_out [N][K] int8 and scales_out [N][K/16] fp32 as
- * rfp2_debug_decode (NaN for both scales of a block with an illegal byte).
+ * product), as its staging threads run it: blocks taken in dword-aligned
+ * 20-byte pairs (the second block of a pair starts at byte 2 of a dword),
+ * the scale mantissas folded into the two int8 operands.  Per block, in
+ * natural weight order: wa_out [N][K] and wb_out [N][K] int8, the operands
+ * whose weight k stands for wa[k] * sA + wb[k] * sB; scales_out
+ * [N][K/32][6] fp32 = (s, -1.5*2^23*s, sA, -1.5*2^23*sA, sB,
+ * -1.5*2^23*sB), where s = sA = sB when the block is one dot product and
+ * s = -sB (negative: the split path) when its halves stay apart; all six
+ * are NaN for a block with an illegal scale byte.
  * Requires N >= 1, K >= 32, K % 32 == 0; w 2-byte aligned, the outputs
  * 4-byte aligned.
  */
-rfp2_status rfp2_debug_decode_i8(const uint8_t* w, int64_t N, int64_t K, int8_t* codes_out,
-                                 float* scales_out, hipStream_t stream);
+rfp2_status rfp2_debug_decode_i8(const uint8_t* w, int64_t N, int64_t K, int8_t* wa_out,
+                                 int8_t* wb_out, float* scales_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

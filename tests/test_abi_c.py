@@ -57,7 +57,7 @@ int main(void) {
   expect("debug_decode", rfp2_debug_decode(p, N_, K_, NULL, p, st), RFP2_E_NULL);
   expect("debug_half_dots", rfp2_debug_half_dots(p, N_, K_, p, 1, NULL, st), RFP2_E_NULL);
   expect("debug_half_sums_mf", rfp2_debug_half_sums_mf(p, N_, K_, p, 1, NULL, st), RFP2_E_NULL);
-  expect("debug_decode_i8", rfp2_debug_decode_i8(p, N_, K_, p, NULL, st), RFP2_E_NULL);
+  expect("debug_decode_i8", rfp2_debug_decode_i8(p, N_, K_, p, p, NULL, st), RFP2_E_NULL);
   expect("debug_decode_f16", rfp2_debug_decode_f16(p, N_, K_, 0, NULL, st), RFP2_E_NULL);
   expect("shape", rfp2_gemv(p, N_, 288, p, p, 1, p, st), RFP2_E_SHAPE);
   expect("align", rfp2_gemv((const uint8_t*)p + 2, N_, K_, p, p, 1, p, st), RFP2_E_ALIGN);

@@ -182,20 +182,72 @@ def test_f16_decode_bitexact(form, N, K):
     assert np.array_equal(got[~bad].view(np.uint16), ref[~bad].view(np.uint16))
 
 
+def exponent_grid_blocks():
+    """Legal blocks for the int8 GEMM's folded decode: blocks 2t and 2t + 1
+    identical (both parities of a pair, as parity_blocks); code bytes
+    (8t + j) % 256; scale pair t covers the exponent pair (E0, E1) =
+    (t // 16, t % 16), every gap 0..15 in both orders, subnormal halves
+    (E = 0) included, with mantissas spread over 0..7 (0..6 at E = 15, where
+    0x7F is illegal).  -> uint8 [512 * 10]."""
+    t = np.repeat(np.arange(256), 2)
+    E0, E1 = t // 16, t % 16
+    M0, M1 = (3 * E0 + E1) % 8, (5 * E1 + E0 + 1) % 8
+    M0 = np.where(E0 == 15, np.minimum(M0, 6), M0)
+    M1 = np.where(E1 == 15, np.minimum(M1, 6), M1)
+    codes = (8 * t[:, None] + np.arange(8)[None, :]) % 256
+    scales = np.stack([8 * E0 + M0, 8 * E1 + M1], axis=1)
+    return np.concatenate([codes, scales], axis=1).astype(np.uint8).reshape(-1)
+
+
+def _decode_i8(packed, N, K):
+    wa, wb = empty((N, K), torch.int8), empty((N, K), torch.int8)
+    sc = empty((N, K // 32, 6), torch.float32)
+    rf.rfp2_debug_decode_i8(to_dev(packed.reshape(-1)), N, K, wa, wb, sc)
+    return host(wa).astype(np.int64), host(wb).astype(np.int64), host(sc).astype(np.float64)
+
+
 @pytest.mark.parametrize("N,K", [(16, 1024), (3, 96), (5, 32)])
-def test_gemm_i8_decode_bitexact_both_blocks_of_a_pair(N, K):
+def test_gemm_i8_folded_decode_bitexact(N, K):
     # the int8 GEMM's staging decode (pairs of blocks, the second one
-    # funnel-shifted), bit for bit: every code byte and every scale byte in
-    # both blocks of a pair; an illegal byte makes both scales of its block NaN
+    # funnel-shifted; the scale mantissas folded into two int8 operands), bit
+    # for bit: every weight's wa * sA + wb * sB is level * scale exactly; a
+    # block is folded whole (s = sA = sB > 0) exactly when its exponents
+    # (E, 0 counted as 1) differ by at most 2, s then the power of two of the
+    # smaller one; otherwise s = -sB and sA, sB are the halves' own powers of
+    # two.  The bias constants are -1.5 * 2^23 times their scales.
     announce("debug_decode_i8", N, K)
-    flat = parity_blocks(256)
-    packed = np.resize(flat, N * K // 32 * 10).reshape(N, K // 32 * 10)
-    codes, scales = empty((N, K), torch.int8), empty((N, K // 16), torch.float32)
-    rf.rfp2_debug_decode_i8(to_dev(packed.reshape(-1)), N, K, codes, scales)
-    codes, scales = host(codes), host(scales)
-    assert np.array_equal(codes, oracle.decoded_int8(packed, N, K))
+    packed = np.resize(exponent_grid_blocks(), N * K // 32 * 10).reshape(N, K // 32 * 10)
+    wa, wb, sc = _decode_i8(packed, N, K)
+    ref = oracle.dequantize_weights(packed, N, K)
+    sA = np.repeat(sc[..., 2], 32, axis=1)
+    sB = np.repeat(sc[..., 4], 32, axis=1)
+    assert np.array_equal(wa * sA + wb * sB, ref)
     _, eb = oracle.unpack_matrix(packed, N, K)
-    ref = _expected_scales(eb)
-    bad_blk = np.repeat(np.isnan(ref).reshape(N, -1, 2).any(axis=2), 2, axis=1)
-    assert np.isnan(scales[bad_blk]).all()
-    assert np.array_equal(scales[~bad_blk], ref[~bad_blk])
+    x = np.maximum(eb.astype(np.int64).reshape(N, K // 32, 2) >> 3, 1)
+    whole = np.abs(x[..., 0] - x[..., 1]) <= 2
+    assert np.array_equal(sc[..., 0] > 0, whole)
+    assert np.array_equal(sc[whole][:, 0], sc[whole][:, 2])
+    assert np.array_equal(sc[whole][:, 0], sc[whole][:, 4])
+    assert np.array_equal(sc[~whole][:, 0], -sc[~whole][:, 4])
+    assert np.array_equal(sc[..., 4], 2.0 ** (x.min(axis=2) - 11))
+    assert np.array_equal(sc[~whole][:, 2], 2.0 ** (x[~whole].max(axis=1) - 11))
+    for v, s_ in ((1, 4), (3, 2), (5, 4)):
+        assert np.array_equal(sc[..., v], -12582912.0 * sc[..., s_])
+    # a whole block's sum stays below 2^22 with any int8 activations
+    assert np.abs(wa + wb).max() <= 240
+    if N * K // 32 >= 512:
+        assert whole.any() and (~whole).any()
+
+
+def test_gemm_i8_decode_illegal_scale_is_nan():
+    # a block with an illegal scale byte (0x7F..0xFF in either half, in
+    # either block of a pair) gets NaN for all six of its scales
+    announce("debug_decode_i8 illegal scale bytes")
+    N, K = 16, 1024
+    packed = np.resize(parity_blocks(256), N * K // 32 * 10).reshape(N, K // 32 * 10)
+    _, _, sc = _decode_i8(packed, N, K)
+    assert np.isnan(sc).all()
+    packed = packed.reshape(N, K // 32, 10)
+    packed[..., 8:10] = np.where(packed[..., 8:10] > 0x7E, 0x38, packed[..., 8:10])
+    _, _, sc = _decode_i8(packed.reshape(N, -1), N, K)
+    assert not np.isnan(sc).any()
