@@ -82,7 +82,7 @@ struct Folded {
 
 // Bytes [-4c, -c, c, 4c] (code 0..3 -> level * c), 0 <= c <= 31.
 __device__ __forceinline__ uint32_t level_table(uint32_t c) {
-  const uint32_t pos = c * 0x10004u;        // 16-bit lanes (4c, c)
+  const uint32_t pos = __umul24(c, 0x10004u); // 16-bit lanes (4c, c)
   const v2s n = v2s{0, 0} - __builtin_bit_cast(v2s, pos);
   return __builtin_amdgcn_perm(pos, __builtin_bit_cast(uint32_t, n), 0x04060200u);
 }

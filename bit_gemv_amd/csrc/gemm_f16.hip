@@ -16,8 +16,8 @@
 //     core's fp32 accumulation may round, each step within 2^-24 of the
 //     running sum;
 //   * the epilogue per (token, row, block) is one FMA, y += d * C, against
-//     four instructions for the int32 per-half partials (a convert and three
-//     FMAs, the first half's convert folded into a biased accumulator).
+//     two for the int8 path's integer block sum (its power-of-two weight
+//     scale and the activation scale, gemm.hip).
 // The rescale, not the matrix cores, bounds the int8 path; here the two are
 // of the same order.
 //
