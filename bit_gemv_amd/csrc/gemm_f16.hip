@@ -7,24 +7,27 @@
 //     with at most 4 significant bits between 2^-10 and 224) and every int8
 //     activation is exactly an fp16 number, and every product is exact in
 //     fp32;
-//   * so the per-half weight scales go into the operands, and one fp16 MFMA
-//     pair (K = 16 each) gives the whole 32-weight block's sum
-//     C = s0 * S0 + s1 * S1 directly in fp32.  It is exact while the two
-//     halves' scale exponents (E, with E = 0 counted as 1) differ by at most
-//     7: every partial sum is an integer multiple of the smaller scale's
-//     unit below 15 * 8128 * (1 + 2^7) < 2^24.  With a wider split the
-//     core's fp32 accumulation may round, each step within 2^-24 of the
-//     running sum;
+//   * so the per-half weight scales go into the operands, and the matrix
+//     core gives the whole 32-weight block's sum C = s0 * S0 + s1 * S1
+//     directly in fp32 (one v_mfma_f32_16x16x32_f16 in the dense kernel, a
+//     pair of v_mfma_f32_32x32x16_f16 in the routed one).  It is exact, in
+//     any summation order, while the two halves' scale exponents (E, with
+//     E = 0 counted as 1) differ by at most 7: every partial sum is an
+//     integer multiple of the smaller scale's unit below
+//     15 * 8128 * (1 + 2^7) < 2^24.  With a wider split the core's fp32
+//     accumulation may round, each step within 2^-24 of the running sum;
 //   * the epilogue per (token, row, block) is one FMA, y += d * C, against
 //     two for the int8 path's integer block sum (its power-of-two weight
 //     scale and the activation scale, gemm.hip).
 // The rescale, not the matrix cores, bounds the int8 path; here the two are
 // of the same order.
 //
-// gfx950 mapping: workgroup tile 128 tokens x 128 rows, four waves of 64 x 64
-// (2 x 2 tiles of v_mfma_f32_32x32x16_f16), K stage of 2 blocks, two LDS
-// buffers with register prefetch of the next stage, XCD-aware tile order
-// (as gemm.hip).  The routed form (tokens sorted by expert, a prompt batch
+// gfx950 mapping: the dense kernel is laid out as gemm.hip (112 x 256 tiles,
+// eight waves, one workgroup per compute unit, 16 x 16 MFMA tiles, K stages
+// of 2 blocks in two LDS buffers with register prefetch, XCD-aware tile
+// order); its 128 x 128 predecessor with 32 x 32 tiles and 448 workgroups
+// (two per compute unit where they fit) took 107.0 us against 97.8 us on
+// 512 x 14336 x 4096 (alternating timings).  The routed form (tokens sorted by expert, a prompt batch
 // through the routed experts) has a kernel of its own below
 // (moe_gemm_kernel): 64-token tiles, each inside one expert's slots, with
 // the weights decoded straight into registers.  Within each 16-weight half
@@ -42,124 +45,122 @@ namespace rfp2 {
 namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int BN = 128;
-constexpr int BKB = 2;                          // blocks per LDS stage
-constexpr int kRowBytes = BKB * 32 * 2 + 16;    // fp16 row of a stage + pad (144)
 constexpr int kXcds = 8;
 
-// TM: 32-token MFMA tiles per wave along the tokens; a workgroup's four waves
-// are 2 (tokens) x 2 (rows), so it covers BM = 64 * TM tokens x 128 rows.
-template <int TM>
+// Dense product: workgroup tile 112 rows x 256 tokens, eight waves (two per
+// SIMD), one workgroup per compute unit (2 x 128 = 256 workgroups on 512 x
+// 14336); wave w owns tokens 32w..32w+31 (two 16-token MFMA tiles) and all
+// seven 16-row tiles.  One v_mfma_f32_16x16x32_f16 is one whole block of one
+// 16 x 16 tile: operand A = the activations (i = token), B = the weights
+// (j = row), so lane l holds row l % 16 and tokens 4 (l / 16) + r, and a
+// block's activation scales are one 16-byte LDS read per token tile.
+constexpr int kRowTiles = 7;
+constexpr int BN = 16 * kRowTiles;              // 112 weight rows
+constexpr int kWaves = 8;
+constexpr int BM = 32 * kWaves;                 // 256 tokens
+constexpr int BKB = 2;                          // blocks per LDS stage
+constexpr int kRowBytes = BKB * 64 + 16;        // fp16 row of a stage + pad (144)
+constexpr int kDecoders = 56;                   // decoding lanes in each of waves 0..3
+
 struct __align__(16) StageF16 {
-  static constexpr int BM = 64 * TM;
-  uint8_t wh[BN * kRowBytes];      // fp16 weights (level * scale)
-  uint8_t ah[BM * kRowBytes];      // fp16 activations
+  uint8_t wh[BN * kRowBytes];      // fp16 weights (level * scale), row r, block b at r*144 + 64b
+  uint8_t ah[BM * kRowBytes];      // fp16 activations, same layout
   float ad[BKB][BM];               // activation scale per (block, token)
 };
 
 struct PrefetchF16 {
-  uint32_t wd[5];                  // the 20-byte block pair holding this thread's block
+  uint32_t wd[5];                  // the 20-byte block pair holding the decoded block
   uint4 a[2];                      // 32 int8 activations
   float d;
 };
 
-// The rows a thread loads, fixed for the whole tile: its weight row (thread
-// -> row tid / 2; both threads of a row load the dword-aligned 20-byte pair
-// of blocks of the stage) and its token's activation row (thread -> token
-// tid / 2, 32-byte block tid % 2 of the stage; only the first 2 * BM threads
-// load activations).
-struct RowPtrs {
+// What a thread stages: block dblk of weight row drow (lanes 0..55 of waves
+// 0..3; two consecutive lanes take the two blocks of one row) and block
+// ablk of token atok (every thread).  Rows / tokens past the end re-read
+// row N-1 / token M-1 (never stored).
+struct RolesF16 {
+  bool dec;
+  int drow, dblk, atok, ablk;
   const uint8_t* w;
   const int8_t* q;
   const float* d;
 };
 
-__device__ __forceinline__ void fetch(PrefetchF16& f, const RowPtrs& r, int kb, int tid,
-                                      bool acts) {
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(r.w + (int64_t)kb * 10);
+__device__ __forceinline__ void fetch(PrefetchF16& f, const RolesF16& r, int kb) {
+  if (r.dec) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(r.w + (int64_t)kb * 10);
 #pragma unroll
-  for (int i = 0; i < 5; ++i) f.wd[i] = src[i];
-  if (acts) {
-    const int ablk = tid & 1;
-    const uint4* asrc = reinterpret_cast<const uint4*>(r.q + (int64_t)(kb + ablk) * 32);
-    f.a[0] = asrc[0];
-    f.a[1] = asrc[1];
-    f.d = r.d[kb + ablk];
+    for (int i = 0; i < 5; ++i) f.wd[i] = src[i];
   }
+  const uint4* asrc = reinterpret_cast<const uint4*>(r.q + (int64_t)kb * 32);
+  f.a[0] = asrc[0];
+  f.a[1] = asrc[1];
+  f.d = r.d[kb];
 }
 
-template <int TM>
-__device__ __forceinline__ void stage_to_lds(const PrefetchF16& f, StageF16<TM>& st, int tid,
-                                             bool acts) {
-  const int wrow = tid >> 1, blk = tid & 1;
-  uint32_t h0[8], h1[8];
-  decode_pair_block_f16(f.wd, blk, h0, h1);
-  uint4* dst = reinterpret_cast<uint4*>(st.wh + wrow * kRowBytes + blk * 64);
-  dst[0] = make_uint4(h0[0], h0[1], h0[2], h0[3]);
-  dst[1] = make_uint4(h0[4], h0[5], h0[6], h0[7]);
-  dst[2] = make_uint4(h1[0], h1[1], h1[2], h1[3]);
-  dst[3] = make_uint4(h1[4], h1[5], h1[6], h1[7]);
-
-  if (acts) {
-    const int arow = tid >> 1, ablk = tid & 1;
-    uint4* adst = reinterpret_cast<uint4*>(st.ah + arow * kRowBytes + ablk * 64);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t X[4] = {f.a[h].x, f.a[h].y, f.a[h].z, f.a[h].w};
-      uint32_t o[8];
-      act_half_f16(X, o);
-      adst[2 * h] = make_uint4(o[0], o[1], o[2], o[3]);
-      adst[2 * h + 1] = make_uint4(o[4], o[5], o[6], o[7]);
-    }
-    st.ad[ablk][arow] = f.d;
+__device__ __forceinline__ void stage_to_lds(const PrefetchF16& f, StageF16& st,
+                                             const RolesF16& r) {
+  if (r.dec) {
+    uint32_t h0[8], h1[8];
+    decode_pair_block_f16(f.wd, r.dblk, h0, h1);
+    uint4* dst = reinterpret_cast<uint4*>(st.wh + r.drow * kRowBytes + r.dblk * 64);
+    dst[0] = make_uint4(h0[0], h0[1], h0[2], h0[3]);
+    dst[1] = make_uint4(h0[4], h0[5], h0[6], h0[7]);
+    dst[2] = make_uint4(h1[0], h1[1], h1[2], h1[3]);
+    dst[3] = make_uint4(h1[4], h1[5], h1[6], h1[7]);
   }
+  uint4* adst = reinterpret_cast<uint4*>(st.ah + r.atok * kRowBytes + r.ablk * 64);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t X[4] = {f.a[h].x, f.a[h].y, f.a[h].z, f.a[h].w};
+    uint32_t o[8];
+    act_half_f16(X, o);
+    adst[2 * h] = make_uint4(o[0], o[1], o[2], o[3]);
+    adst[2 * h + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+  st.ad[r.ablk][r.atok] = f.d;
 }
 
-// Block sums of the stage in sm for this wave's 64 x (32 * TM) (row x token)
-// tile, rescaled by the activation scales and added to acc.  MFMA operand A
-// is the weights (i = row), B the activations (j = token), so every lane
-// holds one token's column of each 32 x 32 tile and the activation scale of
-// a block is one register per tile.
-template <int TM>
-__device__ __forceinline__ void compute_stage(const StageF16<TM>& st, int lane, int wm, int wn,
-                                              v16f (&acc)[2][TM]) {
-  const int koff = 16 * (lane >> 5);            // bytes: 8 fp16 per lane half
+// Block sums of the stage for this wave's 112 rows x 32 tokens, rescaled by
+// the activation scales and added to acc[row tile][token tile].  A block's
+// LDS operands are all read before its first product (one wait per block),
+// and the row tiles are software-pipelined (the products of tile rt + 1 are
+// issued before tile rt is rescaled).
+__device__ __forceinline__ void compute_stage(const StageF16& st, int wave, int lane,
+                                              v4f (&acc)[kRowTiles][2]) {
+  const int g = lane >> 4, li = lane & 15;
 #pragma unroll
   for (int blk = 0; blk < BKB; ++blk) {
-    v8h a[2][2], b[2][TM];                      // [half][tile]
-    float dd[TM];
+    v8h a[2], b[kRowTiles];
+    v4f dv[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        a[h][t] = *reinterpret_cast<const v8h*>(
-            st.wh + (wn * 64 + t * 32 + (lane & 31)) * kRowBytes + blk * 64 + h * 32 + koff);
-#pragma unroll
-    for (int t = 0; t < TM; ++t) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        b[h][t] = *reinterpret_cast<const v8h*>(
-            st.ah + (wm * 32 * TM + t * 32 + (lane & 31)) * kRowBytes + blk * 64 + h * 32 +
-            koff);
-      dd[t] = st.ad[blk][wm * 32 * TM + t * 32 + (lane & 31)];
+    for (int t = 0; t < 2; ++t) {
+      const int tok = 32 * wave + 16 * t;
+      a[t] = *reinterpret_cast<const v8h*>(st.ah + (tok + li) * kRowBytes + blk * 64 + 16 * g);
+      dv[t] = *reinterpret_cast<const v4f*>(&st.ad[blk][tok + 4 * g]);
     }
-    // all tiles' block sums first, then the rescale, so that the FMAs of a
-    // tile do not wait on the matrix-core latency of that same tile
-    v16f c[2][TM];
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn)
+    for (int rt = 0; rt < kRowTiles; ++rt)
+      b[rt] = *reinterpret_cast<const v8h*>(st.wh + (16 * rt + li) * kRowBytes + blk * 64 + 16 * g);
+    v4f c[2][2];
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        c[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[0][tn], b[0][tm], v16f{}, 0, 0, 0);
-        c[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[1][tn], b[1][tm], c[tn][tm], 0, 0, 0);
+    for (int t = 0; t < 2; ++t) c[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], b[0], v4f{}, 0, 0, 0);
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt) {
+      if (rt + 1 < kRowTiles) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          c[(rt + 1) & 1][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], b[rt + 1], v4f{}, 0, 0, 0);
       }
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[tn][tm][r] = fmaf(dd[tm], c[tn][tm][r], acc[tn][tm][r]);
+        for (int r = 0; r < 4; ++r)
+          acc[rt][t][r] = fmaf(dv[t][r], c[rt & 1][t][r], acc[rt][t][r]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -194,14 +195,11 @@ __device__ __forceinline__ int expert_of_tile(const int32_t* tile_start, int E, 
   return seg * chunk + (63 - __clzll(__ballot(v <= i)));
 }
 
-template <int TM>
-__global__ __launch_bounds__(256, 2) void gemm_f16_kernel(GemmF16Params p) {
-  constexpr int BM = 64 * TM;
-  __shared__ StageF16<TM> sm[2];
+__global__ __launch_bounds__(512) void gemm_f16_kernel(GemmF16Params p) {
+  __shared__ StageF16 sm[2];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
   const int N = p.N, K = p.K;
   const int64_t row_bytes = (int64_t)(K / 32) * 10;
   const int nb = K / 32;
@@ -213,70 +211,54 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_kernel(GemmF16Params p) {
     tile = (blockIdx.x % kXcds) * (p.tiles / kXcds) + blockIdx.x / kXcds;
   const int m0 = (tile % p.m_tiles) * BM;
   const int n0 = (tile / p.m_tiles) * BN;
-  const int rows = min(BM, p.M - m0);
 
-  // this thread's load rows; rows past the end re-read a valid row (the
-  // results are never stored)
-  const bool acts = tid < 2 * BM;               // uniform per wave
-  RowPtrs rp;
+  RolesF16 ro;
   {
-    const int wn_row = n0 + (tid >> 1) < N ? n0 + (tid >> 1) : 0;
-    rp.w = p.w + (int64_t)wn_row * row_bytes;
-    const int token = m0 + min(tid >> 1, rows - 1);
-    rp.q = p.q + (int64_t)token * K;
-    rp.d = p.d + (int64_t)token * nb;
+    const int di = kDecoders * wave + lane;
+    ro.dec = wave < 4 && lane < kDecoders;
+    ro.drow = di >> 1;
+    ro.dblk = di & 1;
+    ro.w = p.w + (int64_t)min(n0 + ro.drow, N - 1) * row_bytes;
+    ro.atok = tid >> 1;
+    ro.ablk = tid & 1;
+    const int64_t tok = min(m0 + ro.atok, p.M - 1);
+    ro.q = p.q + tok * K + ro.ablk * 32;
+    ro.d = p.d + tok * nb + ro.ablk;
   }
 
-  v16f acc[2][TM];                              // [row tile][token tile]
+  v4f acc[kRowTiles][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kRowTiles; ++i)
 #pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = v16f{};
+    for (int t = 0; t < 2; ++t) acc[i][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // Software pipeline: iteration s computes stage s from one LDS buffer while
-  // it expands stage s+1 (already in registers) into the other buffer and
-  // loads stage s+2 from memory; a single barrier ends the iteration.  The
-  // buffer written in iteration s was last read in iteration s-1, before the
-  // barrier that ended it.  The loop body has no branch (the last stage is
-  // peeled off and the load of a stage past the end re-reads the last one),
-  // so the matrix-core and vector work of an iteration can be interleaved.
+  // Software pipeline: iteration s computes stage s from one LDS buffer,
+  // then stages s + 1 (already in registers) into the other and loads s + 2
+  // from memory; one barrier per stage.
   PrefetchF16 f;
-  fetch(f, rp, 0, tid, acts);
-  stage_to_lds(f, sm[0], tid, acts);
-  fetch(f, rp, stages > 1 ? BKB : 0, tid, acts);
+  fetch(f, ro, 0);
+  stage_to_lds(f, sm[0], ro);
+  fetch(f, ro, stages > 1 ? BKB : 0);
   __syncthreads();
   for (int s = 0; s + 1 < stages; ++s) {
-    compute_stage(sm[s & 1], lane, wm, wn, acc);
-    stage_to_lds(f, sm[(s + 1) & 1], tid, acts);
-    const int next = s + 2 < stages ? s + 2 : stages - 1;
-    fetch(f, rp, next * BKB, tid, acts);
+    compute_stage(sm[s & 1], wave, lane, acc);
+    stage_to_lds(f, sm[(s + 1) & 1], ro);
+    fetch(f, ro, (s + 2 < stages ? s + 2 : stages - 1) * BKB);
     __syncthreads();
   }
-  compute_stage(sm[(stages - 1) & 1], lane, wm, wn, acc);
+  compute_stage(sm[(stages - 1) & 1], wave, lane, acc);
 
-  // lane -> token, register r -> row n; rows n..n+3 of a register group are
-  // contiguous in y, so whole groups go out as one 16-byte store
-  const bool vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
+  const int g = lane >> 4, li = lane & 15;
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
-    const int m = wm * 32 * TM + tm * 32 + (lane & 31);
-    if (m >= rows) continue;
-    const int out_row = m0 + m;
-    float* yr = p.y + (int64_t)out_row * N;
+  for (int rt = 0; rt < kRowTiles; ++rt) {
+    const int n = n0 + 16 * rt + li;
+    if (n >= N) continue;
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 64 + tn * 32 + 8 * g + 4 * (lane >> 5);
-        const v16f& v = acc[tn][tm];
-        if (vec && n + 3 < N) {
-          *reinterpret_cast<float4*>(yr + n) =
-              make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < N) yr[n + e] = v[4 * g + e];
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 32 * wave + 16 * t + 4 * g + r;
+        if (m < p.M) p.y[(int64_t)m * N + n] = acc[rt][t][r];
       }
   }
 }
@@ -513,14 +495,12 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_kernel(GemmF16Params p) {
 
 hipError_t launch_gemm_f16(const uint8_t* w, int64_t N, int64_t K, const int8_t* q,
                            const float* d, int64_t M, float* y, hipStream_t stream) {
-  constexpr int BM = StageF16<2>::BM;
   GemmF16Params p{};
   p.w = w; p.N = (int)N; p.K = (int)K; p.q = q; p.d = d; p.y = y; p.M = (int)M;
   p.m_tiles = (int)((M + BM - 1) / BM);
   const int n_tiles = (int)((N + BN - 1) / BN);
   p.tiles = p.m_tiles * n_tiles;
-  hipLaunchKernelGGL((gemm_f16_kernel<2>), dim3((uint32_t)p.tiles), dim3(256), 0,
-                     stream, p);
+  hipLaunchKernelGGL(gemm_f16_kernel, dim3((uint32_t)p.tiles), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
