@@ -332,11 +332,26 @@ __global__ __launch_bounds__(512) void gemm_kernel(
   stage_to_lds(f, sm[0], ro);
   fetch(f, ro, stages > 1 ? KB : 0);
   __syncthreads();
-  for (int s = 0; s + 1 < stages; ++s) {
-    compute_stage(sm[s & 1], wave, lane, bias, acc);
-    stage_to_lds(f, sm[(s + 1) & 1], ro);
-    fetch(f, ro, (s + 2 < stages ? s + 2 : stages - 1) * KB);
-    __syncthreads();
+  // Waves 0..3 compute a stage and then stage the next one; waves 4..7 do
+  // it the other way round, so that the two waves of a SIMD are out of
+  // phase: one reads its LDS operands while the other computes (120.8 ->
+  // 113.4 us on 512 x 14336 x 4096; waves 0..3, the decoding ones, staging
+  // first: 117.7 us).  Two copies of the loop, so that the accumulators
+  // never meet a branch.
+  if (wave < 4) {
+    for (int s = 0; s + 1 < stages; ++s) {
+      compute_stage(sm[s & 1], wave, lane, bias, acc);
+      stage_to_lds(f, sm[(s + 1) & 1], ro);
+      fetch(f, ro, (s + 2 < stages ? s + 2 : stages - 1) * KB);
+      __syncthreads();
+    }
+  } else {
+    for (int s = 0; s + 1 < stages; ++s) {
+      stage_to_lds(f, sm[(s + 1) & 1], ro);
+      fetch(f, ro, (s + 2 < stages ? s + 2 : stages - 1) * KB);
+      compute_stage(sm[s & 1], wave, lane, bias, acc);
+      __syncthreads();
+    }
   }
   compute_stage(sm[(stages - 1) & 1], wave, lane, bias, acc);
 
