@@ -59,6 +59,8 @@ KERNEL_SOURCES = ["rfp2_device.h", "gemv_kernel.h", "gemv.hip", "gemv_moe.hip", 
 # the sources of the GEMV kernels (one-token, multi-column and routed forms):
 # a counter record taken on them stays valid while these are unchanged
 GEMV_SOURCES = ["rfp2_device.h", "gemv_kernel.h", "gemv.hip", "gemv_moe.hip", "gemv_m34.hip"]
+# the sources of the routed prompt-batch product (sort + fp16 grouped GEMM)
+MOE_GEMM_SOURCES = ["rfp2_device.h", "f16_decode.h", "gemm_f16.hip", "moe_sort.hip"]
 
 
 def kernel_hash(sources=None) -> str:
@@ -120,10 +122,15 @@ def traffic_from_profiles(workload: str):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_hash") != kernel_hash(rec.get("hash_sources")):
-        return None
     w = rec.get("workloads", {}).get(workload)
-    return w.get("hbm_bytes_per_launch") if w else None
+    if not w:
+        return None
+    # an entry carries the hash of the sources it was taken on (older entries:
+    # the file's GEMV hash)
+    sources = w.get("hash_sources", rec.get("hash_sources"))
+    if w.get("kernel_hash", rec.get("kernel_hash")) != kernel_hash(sources):
+        return None
+    return w.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(cfg, budget_s: float = 12.0) -> dict:
@@ -514,8 +521,22 @@ def measure(workload: str, steps: int, warmup: int, two_launch: bool = False,
         achieved = alg["ops"] / (kern_ms * 1e-3) / 1e12
         # the contraction's own dtype sets the peak: int8 5.0 POP/s, fp16 2.5 PFLOP/s
         peak = I8_PEAK_TOPS if cfg["op"] == "gemm" else F16_PEAK_TFLOPS
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak,
-                "unit": "TOPS" if cfg["op"] == "gemm" else "TFLOP/s", "frac": achieved / peak}
+        compute = {"bound": "mfma", "achieved": achieved, "peak": peak,
+                   "unit": "TOPS" if cfg["op"] == "gemm" else "TFLOP/s",
+                   "frac": achieved / peak}
+        # the roofline's binding limit: ops per algorithmic byte against the
+        # ridge point (peak ops / 8 TB/s).  The dense GEMMs (~1200 ops/B) sit
+        # above it; the routed product, which reads every expert's weights
+        # for ~32 tokens each (~185 ops/B), below it: HBM-bound
+        intensity = alg["ops"] / alg["product_bytes"]
+        ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+        if intensity >= ridge:
+            roof = dict(compute)
+        else:
+            gbs = alg["product_bytes"] / (kern_ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": gbs / HBM_PEAK_GBS, "compute": compute}
+        roof.update(ops_per_byte=intensity, ridge_ops_per_byte=ridge)
     else:
         value = (alg["quant_bytes"] + alg["product_bytes"]) / (ms_step * 1e-3) / 1e9
         unit, metric = "GB/s", "ROCmFP2 GEMV effective HBM GB/s"
@@ -593,7 +614,8 @@ def main(argv=None) -> int:
                           "roofline": {k: s["roofline"][k] for k in
                                        ("bound", "achieved", "peak", "unit", "frac",
                                         "kernel", "kernel_us", "traffic", "ceiling", "warm",
-                                        "cold_isolated")
+                                        "cold_isolated", "compute", "ops_per_byte",
+                                        "ridge_ops_per_byte")
                                        if k in s["roofline"]}})
     if secondary:
         out["secondary"] = secondary

@@ -9,6 +9,10 @@ scaled to bytes by what the same counters read, in the same runs, for the HIP
 runtime's plain device-to-device copy kernel of known size (the bench's
 weight copies); the scale of the largest copies over all runs is used.
 
+Each workload's entry records the hash of the sources of its kernels (the
+GEMV kernels, or those of the routed prompt-batch product); an existing
+OUT_JSON keeps its other workloads' entries.
+
 usage: python -m bit_gemv_amd.hbm_counters OUT_JSON WORKLOAD [WORKLOAD ...]
 """
 from __future__ import annotations
@@ -75,7 +79,8 @@ def main(argv):
                 got[counter] = per_dispatch(run_pass(wl, counter, tmp), counter)
             finally:
                 shutil.rmtree(tmp, ignore_errors=True)
-        prods = {n: v for n, v in got["FETCH_SIZE"].items() if "gemv_kernel" in n}
+        prods = {n: v for n, v in got["FETCH_SIZE"].items()
+                 if "gemv_kernel" in n or "moe_gemm_kernel" in n}
         kernel = max(prods, key=lambda n: len(prods[n]))
         fetch = statistics.median(got["FETCH_SIZE"][kernel])
         write = statistics.median(got["WRITE_SIZE"][kernel])
@@ -84,9 +89,11 @@ def main(argv):
                 big = [x for x in v if x > 0.9 * max(v)]
                 wv = [x for x in got["WRITE_SIZE"].get(n, []) if x > 0.9 * max(got["WRITE_SIZE"][n])]
                 copies.append((per_copy, statistics.median(big), statistics.median(wv)))
+        sources = bench.MOE_GEMM_SOURCES if cfg["op"] == "moe_gemm" else bench.GEMV_SOURCES
         res[wl] = {"kernel": kernel, "dispatches": len(got["FETCH_SIZE"][kernel]),
                    "fetch_kib_median": fetch, "write_kib_median": write,
-                   "algorithmic_bytes_per_launch": alg["product_bytes"]}
+                   "algorithmic_bytes_per_launch": alg["product_bytes"],
+                   "kernel_hash": bench.kernel_hash(sources), "hash_sources": sources}
     nbytes, f_copy, w_copy = max(copies)
     rf, wf = nbytes / 1024 / f_copy, nbytes / 1024 / w_copy
     for wl, r in res.items():
@@ -94,7 +101,14 @@ def main(argv):
         wr = round(r["write_kib_median"] * 1024 * wf)
         r.update(hbm_read_bytes_per_launch=rd, hbm_write_bytes_per_launch=wr,
                  hbm_bytes_per_launch=rd + wr,
-                 ratio_to_algorithmic=(rd + wr) / r["algorithmic_bytes_per_launch"])
+                 ratio_to_algorithmic=(rd + wr) / r["algorithmic_bytes_per_launch"],
+                 read_factor=rf, write_factor=wf)
+    try:
+        with open(out_json) as f:
+            kept = json.load(f).get("workloads", {})
+    except (OSError, ValueError):
+        kept = {}
+    res = {**kept, **res}
     out = {"copy_calibration": {"kernel": "__amd_rocclr_copyBuffer", "bytes": nbytes,
                                 "fetch_kib": f_copy, "write_kib": w_copy,
                                 "read_factor": rf, "write_factor": wf},
