@@ -173,10 +173,14 @@ __device__ __forceinline__ void fetch(Prefetch& f, const Roles& r, int kb) {
   f.d = r.d[kb];
 }
 
-__device__ __forceinline__ void stage_to_lds(const Prefetch& f, Stage& st, const Roles& r) {
+__device__ __forceinline__ void stage_to_lds(const Prefetch& f, Stage& st, const Roles& r,
+                                             uint32_t* split) {
   if (r.dec) {
     Folded fb;
     fold_pair_member(f.wd, r.dblk, fb);
+    // the row tile of a block whose halves stay apart (or NaN) takes the
+    // split path: one bit per (block, row tile)
+    if (!(fb.sm.x > 0.0f)) atomicOr(&split[r.dblk], 1u << (r.drow >> 4));
     uint4* dst = reinterpret_cast<uint4*>(st.w + r.drow * kWRow + r.dblk * 64);
     dst[0] = make_uint4(fb.wa[0][0], fb.wa[0][1], fb.wa[0][2], fb.wa[0][3]);
     dst[1] = make_uint4(fb.wa[1][0], fb.wa[1][1], fb.wa[1][2], fb.wa[1][3]);
@@ -237,14 +241,18 @@ __device__ __forceinline__ void split_sums(const Stage& st, int blk, int rt, int
 // first (one wait per block instead of one per tile), then the tiles are
 // software-pipelined (the MFMAs of tile rt + 1 are issued before tile rt is
 // rescaled).  Every tile takes the folded form first; a tile that needs the
-// split form (s <= 0 or NaN on one of its rows, rare) has its u recomputed
-// in a branch that touches nothing else, so the accumulators never meet a
-// branch (where the compiler would copy them).
-__device__ __forceinline__ void compute_stage(const Stage& st, int wave, int lane,
-                                              const v4i& bias, v4f (&acc)[kRowTiles][2]) {
+// split form (s <= 0 or NaN on one of its rows, rare; the staging lanes set
+// its bit in `split`, one scalar test per tile instead of a vector compare:
+// 111.9 -> 109.5 us) has its u recomputed in a branch that touches nothing
+// else, so the accumulators never meet a branch (where the compiler would
+// copy them).
+__device__ __forceinline__ void compute_stage(const Stage& st, const uint32_t* split, int wave,
+                                              int lane, const v4i& bias,
+                                              v4f (&acc)[kRowTiles][2]) {
   const int g = lane >> 4, li = lane & 15;
 #pragma unroll
   for (int blk = 0; blk < KB; ++blk) {
+    const uint32_t tiles_split = __builtin_amdgcn_readfirstlane(split[blk]);
     v4i a[2], b[kRowTiles];
     v4f dv[2];
     float2 s[kRowTiles];
@@ -271,7 +279,7 @@ __device__ __forceinline__ void compute_stage(const Stage& st, int wave, int lan
       }
       float u[2][4];
       folded_sums(P[rt & 1], s[rt], u);
-      if (__builtin_expect(__ballot(!(s[rt].x > 0.0f)) != 0, 0))
+      if (__builtin_expect((tiles_split >> rt) & 1u, 0))
         split_sums(st, blk, rt, g, li, bias, a, P[rt & 1], u);
       accumulate(dv, u, acc[rt]);
       // keep the update here: sunk to the end of the block, the seven
@@ -286,6 +294,10 @@ __global__ __launch_bounds__(512) void gemm_kernel(
     const uint8_t* __restrict__ w, int N, int K, const int8_t* __restrict__ q,
     const float* __restrict__ d, int M, float* __restrict__ y, int m_tiles, int tiles) {
   __shared__ Stage sm[2];
+  // split-path flags of stage s in slot s % 4: set while staging (iteration
+  // s - 1), read while computing (iteration s), cleared in iteration s + 2;
+  // barriers separate all three
+  __shared__ uint32_t split[4][KB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -331,19 +343,22 @@ __global__ __launch_bounds__(512) void gemm_kernel(
   // (the stage count K / 64 is a multiple of 4).  Iteration s computes
   // stage s, stages s + 1 from the set loaded two iterations earlier and
   // reloads that set with stage s + 3 (past the end: the last stage again).
+  if (tid < 4 * KB) split[tid / KB][tid % KB] = 0u;
+  __syncthreads();
   Prefetch f0, f1;
   fetch(f0, ro, 0);
   fetch(f1, ro, KB);
-  stage_to_lds(f0, sm[0], ro);
+  stage_to_lds(f0, sm[0], ro, split[0]);
   fetch(f0, ro, 2 * KB);
   __syncthreads();
   const int last = (stages - 1) * KB;
 #define RFP2_GEMM_STEP(S, FN, COMPUTE_FIRST)                                   \
   {                                                                             \
-    if (COMPUTE_FIRST) compute_stage(sm[(S) & 1], wave, lane, bias, acc);       \
-    stage_to_lds(FN, sm[((S) + 1) & 1], ro);                                    \
+    if (COMPUTE_FIRST) compute_stage(sm[(S) & 1], split[(S) & 3], wave, lane, bias, acc); \
+    stage_to_lds(FN, sm[((S) + 1) & 1], ro, split[((S) + 1) & 3]);              \
     fetch(FN, ro, min(((S) + 3) * KB, last));                                   \
-    if (!(COMPUTE_FIRST)) compute_stage(sm[(S) & 1], wave, lane, bias, acc);    \
+    if (!(COMPUTE_FIRST)) compute_stage(sm[(S) & 1], split[(S) & 3], wave, lane, bias, acc); \
+    if (tid < KB) split[((S) + 2) & 3][tid] = 0u;                               \
     __syncthreads();                                                            \
   }
   // Waves 0..3 compute a stage and then stage the next one; waves 4..7 do
@@ -368,11 +383,11 @@ __global__ __launch_bounds__(512) void gemm_kernel(
   // the last two stages: stage s = stages - 2 computes and stages the last
   {
     const int s = stages - 2;
-    compute_stage(sm[s & 1], wave, lane, bias, acc);
-    stage_to_lds(f1, sm[(s + 1) & 1], ro);
+    compute_stage(sm[s & 1], split[s & 3], wave, lane, bias, acc);
+    stage_to_lds(f1, sm[(s + 1) & 1], ro, split[(s + 1) & 3]);
     __syncthreads();
   }
-  compute_stage(sm[(stages - 1) & 1], wave, lane, bias, acc);
+  compute_stage(sm[(stages - 1) & 1], split[(stages - 1) & 3], wave, lane, bias, acc);
 
   const int g = lane >> 4, li = lane & 15;
 #pragma unroll
