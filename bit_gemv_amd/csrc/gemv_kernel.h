@@ -380,6 +380,70 @@ __device__ __forceinline__ void load_acts2_and_chunk(const float* abase, uint32_
       : "memory");
 }
 
+// The routed quantizing form splits the above in two, so that the expert id
+// (a scalar load, on which the weight address depends) is awaited only once
+// the activation loads are out: first the activation loads alone, then --
+// the expert known -- the barrier, the weight chunk and the wait for the
+// activations.  The registers the first asm fills are in-out operands of
+// the second, so nothing reads them in between.
+__device__ __forceinline__ void load_acts(const float* abase, uint32_t aoff, v4f (&x)[4]) {
+  asm volatile(
+      "global_load_dwordx4 %0, %4, %5\n\t"
+      "global_load_dwordx4 %1, %4, %5 offset:16\n\t"
+      "global_load_dwordx4 %2, %4, %5 offset:32\n\t"
+      "global_load_dwordx4 %3, %4, %5 offset:48"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+      : "v"(aoff), "s"(abase)
+      : "memory");
+}
+__device__ __forceinline__ void load_acts2(const float* abase, uint32_t aoff0, uint32_t aoff1,
+                                           v4f (&x)[4], v4f (&z)[4]) {
+  asm volatile(
+      "global_load_dwordx4 %0, %8, %10\n\t"
+      "global_load_dwordx4 %1, %8, %10 offset:16\n\t"
+      "global_load_dwordx4 %2, %8, %10 offset:32\n\t"
+      "global_load_dwordx4 %3, %8, %10 offset:48\n\t"
+      "global_load_dwordx4 %4, %9, %10\n\t"
+      "global_load_dwordx4 %5, %9, %10 offset:16\n\t"
+      "global_load_dwordx4 %6, %9, %10 offset:32\n\t"
+      "global_load_dwordx4 %7, %9, %10 offset:48"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(z[0]), "=&v"(z[1]),
+        "=&v"(z[2]), "=&v"(z[3])
+      : "v"(aoff0), "v"(aoff1), "s"(abase)
+      : "memory");
+}
+__device__ __forceinline__ void chunk_after_acts(const uint8_t* wbase, const ChunkOffsets& o,
+                                                 uint32_t m0v, v4f (&x)[4]) {
+  asm volatile(
+      "s_barrier\n\t"
+      "s_mov_b32 m0, %9\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, %10\n\t"
+      "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %10\n\t"
+      "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, %10\n\t"
+      "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %7, %10\n\t"
+      "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %8, %10\n\t"
+      "s_waitcnt vmcnt(5)"
+      : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])
+      : "v"(o.off[0]), "v"(o.off[1]), "v"(o.off[2]), "v"(o.off[3]), "v"(o.off[4]), "s"(m0v),
+        "s"(wbase)
+      : "memory");
+}
+__device__ __forceinline__ void chunk_after_acts2(const uint8_t* wbase, const ChunkOffsets& o,
+                                                  uint32_t m0v, v4f (&x)[4], v4f (&z)[4]) {
+  asm volatile(
+      "s_barrier\n\t"
+      "s_mov_b32 m0, %13\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %8, %14\n\t"
+      "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %9, %14\n\t"
+      "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %10, %14\n\t"
+      "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %11, %14\n\t"
+      "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %12, %14\n\t"
+      "s_waitcnt vmcnt(5)"
+      : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(z[0]), "+v"(z[1]), "+v"(z[2]),
+        "+v"(z[3])
+      : "v"(o.off[0]), "v"(o.off[1]), "v"(o.off[2]), "v"(o.off[3]), "v"(o.off[4]), "s"(m0v),
+        "s"(wbase)
+      : "memory");
+}
+
 // Quantize the 16 fp32 activations of one half in place of the separate
 // activation kernel, with its exact arithmetic: the block's max |a| comes
 // from this lane and its partner (the other half of the block, lane ^ 1),
@@ -554,9 +618,10 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
   int col_tok[M], col_out[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) col_tok[m] = col_out[m] = m;
+  int e = 0;                                    // the slot's expert (MoE form)
   if (MOE) {
     const int s0 = blockIdx.y;
-    const int e = p.ids[s0];
+    e = p.ids[s0];
     col_tok[0] = s0 / p.top_k;
     col_out[0] = s0;
     if (M > 1) {
@@ -580,10 +645,14 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
         }
       }
     }
-    id_ok = e >= 0 && e < p.E;
-    wb = p.w + (int64_t)(id_ok ? e : 0) * (int64_t)N * row_bytes;
+    // the expert selects the weight matrix (the quantizing form does this
+    // once its activation loads are out, below)
+    if constexpr (!QA) {
+      id_ok = e >= 0 && e < p.E;
+      wb = p.w + (int64_t)(id_ok ? e : 0) * (int64_t)N * row_bytes;
+    }
   }
-  wb += (int64_t)row0 * row_bytes;
+  if constexpr (!(MOE && QA)) wb += (int64_t)row0 * row_bytes;
 
   // per-wave LDS: JT chunk buffers of 1280 dwords, then this wave's
   // activations (M columns x ag = J*L groups of kGroupPieces pieces) and
@@ -654,12 +723,28 @@ __global__ __launch_bounds__(512) void gemv_kernel(Params p) {
       aoffs[r] = (group_of(hs[r] >> 4) * 256 + (hs[r] & 15) * 16) * 4;
     }
     v4f x[QH][4];
-    if constexpr (QH == 1)
+    if constexpr (MOE) {
+      // the expert id is awaited after the activation loads are issued (its
+      // scalar load's latency then overlaps theirs); the empty asm keeps
+      // every use of it below the first asm
+      if constexpr (QH == 1)
+        load_acts(p.a, (uint32_t)aoffs[0], x[0]);
+      else
+        load_acts2(p.a, (uint32_t)aoffs[0], (uint32_t)aoffs[QH - 1], x[0], x[QH - 1]);
+      asm volatile("" : "+s"(e));
+      id_ok = e >= 0 && e < p.E;
+      wb = p.w + (int64_t)(id_ok ? e : 0) * (int64_t)N * row_bytes + (int64_t)row0 * row_bytes;
+      if constexpr (QH == 1)
+        chunk_after_acts(wb + (int64_t)(wave << ls) * 80, co, ring_m0, x[0]);
+      else
+        chunk_after_acts2(wb + (int64_t)(wave << ls) * 80, co, ring_m0, x[0], x[QH - 1]);
+    } else if constexpr (QH == 1) {
       load_acts_and_chunk(p.a, (uint32_t)aoffs[0], wb + (int64_t)(wave << ls) * 80, co,
                           ring_m0, x[0]);
-    else
+    } else {
       load_acts2_and_chunk(p.a, (uint32_t)aoffs[0], (uint32_t)aoffs[QH - 1],
                            wb + (int64_t)(wave << ls) * 80, co, ring_m0, x[0], x[QH - 1]);
+    }
 #pragma unroll
     for (int r = 0; r < QH; ++r) {
       uint32_t A[4];
