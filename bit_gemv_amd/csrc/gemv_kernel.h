@@ -449,8 +449,9 @@ __device__ __forceinline__ void chunk_after_acts2(const uint8_t* wbase, const Ch
 // from this lane and its partner (the other half of the block, lane ^ 1),
 // d = fl32(max / 127) (IEEE division), q = roundf(fl32(a / d)) (halves away
 // from zero), d = NaN and q = 0 for a block with a non-finite value, q = 0
-// when d = 0.  |a / d| <= 127 * (1 + 2^-23), so q never needs the clamp to
-// +-127.
+// when d = 0, q clamped to +-127.  For a normal d, |a / d| <= 127 * (1 +
+// 2^-23) and the clamp never acts; a subnormal d keeps fewer significant
+// bits, and a / d reaches up to ~190 when max |a| is below ~2.2e-41.
 //   * fl32(a / d) is replaced by t = a * rcp(d); adding 1.5 * 2^23 rounds t
 //     to the nearest integer k and leaves k's two's-complement low byte in
 //     the low byte of the sum.  Error budget, with |a / d| <= 127 * (1 +
@@ -462,7 +463,8 @@ __device__ __forceinline__ void chunk_after_acts2(const uint8_t* wbase, const Ch
 //     |t - k| < 0.49997 = 0.5 - 3e-5, fl32(a / d) lies strictly within 0.5 of
 //     k: k is roundf(fl32(a / d)).
 //   * Otherwise (t within 3e-5 of a half-integer), or when d is subnormal,
-//     the lane redoes its values with the IEEE division and roundf.
+//     the lane redoes its values with the IEEE division, the clamp and
+//     roundf.
 // A receives q packed four per dword in the lane order of the expanded
 // weights (A[i] = q[i], q[4+i], q[8+i], q[12+i]: packing in that order costs
 // the same as packing in natural order and saves the transpose); returns d.
@@ -519,7 +521,7 @@ __device__ __forceinline__ float quantize_half(const v4f (&x)[4], uint32_t (&A)[
   if (need_exact) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      u[i] = __float_as_uint(roundf(__fdiv_rn(v[i], dv)) + kMagic);
+      u[i] = __float_as_uint(roundf(fminf(fmaxf(__fdiv_rn(v[i], dv), -127.0f), 127.0f)) + kMagic);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) A[i] = pack_low_bytes(u[i], u[4 + i], u[8 + i], u[12 + i]);

@@ -18,13 +18,15 @@ import oracle
 import synth
 from _gpu import announce, assert_within_bound, empty, host, to_dev, torch
 from test_gpu_decode import random_blocks
+from test_oracle_acts import deep_subnormal_block
 
 pytestmark = pytest.mark.gpu
 
 
 def boundary_activations(K: int, seed: int) -> np.ndarray:
     """fp32 [K]: normal draws, with blocks of ties, near-ties, zeros, a NaN,
-    an infinity and a subnormal scale scattered over it."""
+    an infinity and subnormal scales (some of them clamping) scattered over
+    it."""
     rng = np.random.default_rng(seed)
     a = rng.standard_normal(K).astype(np.float32)
     nb = K // 32
@@ -43,7 +45,10 @@ def boundary_activations(K: int, seed: int) -> np.ndarray:
         elif kind == 2:   # all zeros: d = 0, q = 0
             blk[:] = 0.0
         elif kind == 3:   # tiny values: the scale is a subnormal number
-            blk[:] = (rng.standard_normal(32) * 1e-37).astype(np.float32)
+            if (b // 42) % 2:   # so small that only the clamp keeps q at 127
+                blk[:] = deep_subnormal_block()
+            else:
+                blk[:] = (rng.standard_normal(32) * 1e-37).astype(np.float32)
         elif kind == 4:   # a NaN poisons the block
             blk[rng.integers(0, 32)] = np.nan
         else:             # an infinity too

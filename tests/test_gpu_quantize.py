@@ -6,6 +6,7 @@ import bit_gemv_amd as rf
 import oracle
 import synth
 from _gpu import announce, empty, host, sample_rows, to_dev, torch
+from test_oracle_acts import deep_subnormal_block
 
 pytestmark = pytest.mark.gpu
 
@@ -27,6 +28,8 @@ def test_quantize_acts_bitexact(M, K):
         a[0, 32:64] = np.arange(32, dtype=np.float32) - 15.5  # d = 1: a/d ends in .5
         a[0, 63] = 127.0
         a[-1, 64:96] *= np.float32(1e-30)                  # tiny values
+    if K >= 128:
+        a[0, 96:128] = deep_subnormal_block()               # clamped quotients
     q_ref, d_ref = oracle.quantize_acts(a)
     q, d = _gpu_quantize_acts(a)
     assert np.array_equal(d.view(np.uint32), d_ref.view(np.uint32))

@@ -94,6 +94,21 @@ def test_zero_and_underflowing_blocks():
     assert np.all(d == 0) and np.all(q == 0)
 
 
+def deep_subnormal_block():
+    """32 activations n * 2^-149 with max n = 1327, so max / 127 = 10.449 *
+    2^-149 rounds to the subnormal d = 10 * 2^-149 and the largest quotient
+    is 132.7: past 127.5, where only the clamp keeps q at 127."""
+    n = np.array([1327, 700, -1000, 3, -5, 1200, -1327, 0] * 4, np.float32)
+    return n * np.float32(2.0 ** -149)
+
+
+def test_subnormal_scale_quotients_are_clamped():
+    q, d = oracle.quantize_acts(deep_subnormal_block()[None, :])
+    assert d[0, 0] == np.float32(10 * 2.0 ** -149)
+    # q = clamp(round(n / 10)), halves away from zero
+    assert list(q[0, :8]) == [127, 70, -100, 0, -1, 120, -127, 0]
+
+
 def test_rejects_bad_input():
     with pytest.raises(ValueError):
         oracle.quantize_acts(np.full((1, 32), np.inf, np.float32))
