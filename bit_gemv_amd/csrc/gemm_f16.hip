@@ -304,14 +304,16 @@ struct __align__(16) MoeStage {
   float ad[kMoeKB][kMoeTokens];
 };
 
-__device__ __forceinline__ void load_pair(WPair& w, const uint8_t* row, int kb) {
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(row + (int64_t)kb * 10);
-  w.d0 = src[0];
-  w.d1 = src[1];
-  w.d2 = src[2];
-  w.d3 = src[3];
-  w.d4 = src[4];
+// A stage's 8 blocks of one weight row are 80 contiguous bytes, 16-byte
+// aligned (a row is a whole number of 80-byte groups): five 16-byte loads.
+// Pair p of blocks (2p, 2p + 1) is dwords 5p .. 5p + 4 of them.
+__device__ __forceinline__ void load_quad(uint4& x, const uint8_t* row, int kb, int k) {
+  x = reinterpret_cast<const uint4*>(row + (int64_t)kb * 10)[k];
 }
+__device__ __forceinline__ WPair pair0(const uint4 (&W)[5]) { return {W[0].x, W[0].y, W[0].z, W[0].w, W[1].x}; }
+__device__ __forceinline__ WPair pair1(const uint4 (&W)[5]) { return {W[1].y, W[1].z, W[1].w, W[2].x, W[2].y}; }
+__device__ __forceinline__ WPair pair2(const uint4 (&W)[5]) { return {W[2].z, W[2].w, W[3].x, W[3].y, W[3].z}; }
+__device__ __forceinline__ WPair pair3(const uint4 (&W)[5]) { return {W[3].w, W[4].x, W[4].y, W[4].z, W[4].w}; }
 
 // One block of a stage's activations for one thread: token t % 64, block
 // t / 64 (threads 0..511); in a tile of at most 32 slots, token t % 32 and
@@ -424,11 +426,9 @@ __global__ __launch_bounds__(64 * kMoeWaves) void moe_gemm_kernel(GemmF16Params 
   const float* drow = p.d + (int64_t)token * nb + ab;
 
   v16f acc[2] = {v16f{}, v16f{}};
-  WPair w0, w1, w2, w3;                         // the stage's four pairs of blocks
-  load_pair(w0, wrow, 0);
-  load_pair(w1, wrow, 2);
-  load_pair(w2, wrow, 4);
-  load_pair(w3, wrow, 6);
+  uint4 W[5];                                   // the stage's 80 bytes of this row
+#pragma unroll
+  for (int k = 0; k < 5; ++k) load_quad(W[k], wrow, 0, k);
   ActBlock ap;
 
   // Per stage: this stage's activations (loaded during the previous one) go
@@ -463,14 +463,14 @@ __global__ __launch_bounds__(64 * kMoeWaves) void moe_gemm_kernel(GemmF16Params 
     v16f c[2];                                                                       \
     v8h a0, a1;                                                                      \
     moe_b(sm, 0, lane, TWO, bx);                                                     \
-    decode_half<0>(w0, kh, a0, a1);                                                  \
-    RFP2_MOE_STEP(TWO, 0, bx, by, decode_half<1>(w0, kh, a0, a1); load_pair(w0, wrow, kb_next + 0)) \
-    RFP2_MOE_STEP(TWO, 1, by, bx, decode_half<0>(w1, kh, a0, a1))                   \
-    RFP2_MOE_STEP(TWO, 2, bx, by, decode_half<1>(w1, kh, a0, a1); load_pair(w1, wrow, kb_next + 2)) \
-    RFP2_MOE_STEP(TWO, 3, by, bx, decode_half<0>(w2, kh, a0, a1))                   \
-    RFP2_MOE_STEP(TWO, 4, bx, by, decode_half<1>(w2, kh, a0, a1); load_pair(w2, wrow, kb_next + 4)) \
-    RFP2_MOE_STEP(TWO, 5, by, bx, decode_half<0>(w3, kh, a0, a1))                   \
-    RFP2_MOE_STEP(TWO, 6, bx, by, decode_half<1>(w3, kh, a0, a1); load_pair(w3, wrow, kb_next + 6)) \
+    decode_half<0>(pair0(W), kh, a0, a1);                                            \
+    RFP2_MOE_STEP(TWO, 0, bx, by, decode_half<1>(pair0(W), kh, a0, a1); load_quad(W[0], wrow, kb_next, 0)) \
+    RFP2_MOE_STEP(TWO, 1, by, bx, decode_half<0>(pair1(W), kh, a0, a1))             \
+    RFP2_MOE_STEP(TWO, 2, bx, by, decode_half<1>(pair1(W), kh, a0, a1); load_quad(W[1], wrow, kb_next, 1)) \
+    RFP2_MOE_STEP(TWO, 3, by, bx, decode_half<0>(pair2(W), kh, a0, a1))             \
+    RFP2_MOE_STEP(TWO, 4, bx, by, decode_half<1>(pair2(W), kh, a0, a1); load_quad(W[2], wrow, kb_next, 2)) \
+    RFP2_MOE_STEP(TWO, 5, by, bx, decode_half<0>(pair3(W), kh, a0, a1))             \
+    RFP2_MOE_STEP(TWO, 6, bx, by, decode_half<1>(pair3(W), kh, a0, a1); load_quad(W[3], wrow, kb_next, 3); load_quad(W[4], wrow, kb_next, 4)) \
     RFP2_MOE_STEP(TWO, 7, by, bx, (void)0)                                          \
   }
   if (two) {
