@@ -195,6 +195,94 @@ __device__ __forceinline__ int expert_of_tile(const int32_t* tile_start, int E, 
   return seg * chunk + (63 - __clzll(__ballot(v <= i)));
 }
 
+// Exclusive prefix sum over the 64 lanes of a wave; `total` gets the sum.
+__device__ __forceinline__ int wave_exclusive_sum(int v, int lane, int& total) {
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(inc, d);
+    if (lane >= d) inc += u;
+  }
+  total = __shfl(inc, 63);
+  return inc - v;
+}
+
+// Slots of expert e (0 when e >= E): offsets has E + 1 entries.
+__device__ __forceinline__ int expert_slots(const int32_t* offsets, int E, int e) {
+  return offsets[min(e + 1, E)] - offsets[min(e, E)];
+}
+
+constexpr int kRankedExperts = 256;             // tile_of_rank: C <= 4
+
+// Long tiles (more than 32 slots) and short ones among the experts
+// lane + 64 j, j < C (C = ceil(E / 64) <= 4): expert e with n slots has
+// (n + 31) / 64 long tiles and ceil(n / 64) in all.  Consecutive lanes read
+// consecutive offsets, and every load is issued before the first is used.
+
+__device__ __forceinline__ void lane_tiles(const int32_t* offsets, int E, int lane, int C,
+                                           int& hs, int& ls) {
+  int n[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) n[j] = j < C ? expert_slots(offsets, E, 64 * j + lane) : 0;
+  hs = 0;
+  ls = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = (n[j] + 31) >> 6;
+    hs += h;
+    ls += ((n[j] + 63) >> 6) - h;
+  }
+}
+
+// Routed tile of rank i.  A tile of more than 32 slots runs two 32-token
+// MFMA tiles (twice the matrix-core and rescale work of a smaller one), so
+// ranks 0 .. H-1 are the tiles of more than 32 slots (an expert's full
+// tiles, then its last tile if that holds more than 32 slots) and ranks
+// H .. the experts' last tiles of 1 .. 32 slots.  Workgroups start in rank
+// order: the long tiles start first and the short ones fill in behind them,
+// instead of two long tiles meeting on one compute unit at the end.  Within
+// each kind the order is lane-major over the experts lane + 64 j: one
+// wave-wide scan of the lanes' counts finds the lane holding rank i, a
+// second over that lane's experts (at most 4) the expert.  For E <= 256
+// only: with more experts each wave's loads of the counts (two per 64
+// experts) took longer than the reordering gained (2048 experts of 256 x 512
+// with one slot each: 62 -> 93 us), and tiles keep the sort's order there.
+// -> e, and t, the tile's index among the expert's ceil(n / 64) tiles (the
+// count tile_start holds); e = -1 only for a rank past the last tile.
+__device__ __forceinline__ void tile_of_rank(const int32_t* offsets, int E, int i, int lane,
+                                             int& e_out, int& t_out) {
+  const int C = (E + 63) >> 6;
+  int hs, ls;
+  lane_tiles(offsets, E, lane, C, hs, ls);
+  int H, L;
+  const int hbase = wave_exclusive_sum(hs, lane, H);
+  const int lbase = wave_exclusive_sum(ls, lane, L);
+  const bool heavy = i < H;                     // uniform
+  const int tgt = heavy ? i : i - H;
+  const int base = heavy ? hbase : lbase;
+  const int cnt = heavy ? hs : ls;
+  const uint64_t hit = __ballot(cnt > 0 && tgt >= base && tgt < base + cnt);
+  const int src = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
+  const int B = __shfl(base, src);
+  int c = 0, h = 0;
+  if (lane < C) {
+    const int n = expert_slots(offsets, E, src + 64 * lane);
+    h = (n + 31) >> 6;
+    c = heavy ? h : ((n + 63) >> 6) - h;
+  }
+  int all;
+  const int ex = B + wave_exclusive_sum(c, lane, all);
+  const uint64_t hit2 = __ballot(c > 0 && tgt >= ex && tgt < ex + c);
+  if (hit == 0 || hit2 == 0) {
+    e_out = -1;
+    t_out = 0;
+    return;
+  }
+  const int jj = __ffsll((unsigned long long)hit2) - 1;
+  e_out = src + 64 * jj;
+  t_out = heavy ? tgt - __shfl(ex, jj) : __shfl(h, jj);
+}
+
 __global__ __launch_bounds__(512) void gemm_f16_kernel(GemmF16Params p) {
   __shared__ StageF16 sm[2];
   const int tid = threadIdx.x;
@@ -401,13 +489,21 @@ __global__ __launch_bounds__(64 * kMoeWaves) void moe_gemm_kernel(GemmF16Params 
   const int nb = K / 32;
   const int nst = nb / kMoeKB;                  // K % 256 == 0
 
-  // token tile i runs on XCD i % 8 with all of its row tiles (its gathered
-  // activations stay in that XCD's L2); workgroups past the last tile leave
+  // token tile of rank i runs on XCD i % 8 with all of its row tiles (its
+  // gathered activations stay in that XCD's L2), tiles of more than 32 slots
+  // first up to 256 experts; workgroups past the last tile leave
   const int x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
   const int i = kXcds * (k / p.n_tiles) + x;
   if (i >= p.tile_start[p.E]) return;
-  const int e = expert_of_tile(p.tile_start, p.E, i, lane);
-  const int start = p.offsets[e] + (i - p.tile_start[e]) * kMoeTokens;
+  int e, t;
+  if (p.E <= kRankedExperts) {
+    tile_of_rank(p.offsets, p.E, i, lane, e, t);
+    if (e < 0) return;                          // uniform
+  } else {
+    e = expert_of_tile(p.tile_start, p.E, i, lane);
+    t = i - p.tile_start[e];
+  }
+  const int start = p.offsets[e] + t * kMoeTokens;
   const int rows = min(kMoeTokens, p.offsets[e + 1] - start);
   const int n0 = (k % p.n_tiles) * kMoeRows;
   const bool two = rows > 32;                   // uniform

@@ -116,7 +116,13 @@ def test_moe_gemm_against_oracle_and_dense(T, top_k, K, kind):
 
 
 @pytest.mark.parametrize("E,T,top_k,K,N", [(2048, 4096, 2, 256, 130),   # long sort chunks
-                                          (40, 300, 2, 16384, 200)])     # 64 stages of K
+                                          (40, 300, 2, 16384, 200),      # 64 stages of K
+                                          # tiles of more than 32 slots started first:
+                                          # 2 .. 4 groups of 64 experts, then the
+                                          # first expert count that keeps the sort's order
+                                          (130, 1200, 4, 512, 200),
+                                          (256, 2048, 8, 256, 130),
+                                          (257, 1024, 4, 256, 130)])
 def test_moe_gemm_large_shapes_against_dense(E, T, top_k, K, N):
     # every routed row bit for bit against rfp2_gemm_f16 of its expert, and
     # sampled rows against the oracle
