@@ -61,6 +61,9 @@ KERNEL_SOURCES = ["rfp2_device.h", "gemv_kernel.h", "gemv.hip", "gemv_moe.hip", 
 GEMV_SOURCES = ["rfp2_device.h", "gemv_kernel.h", "gemv.hip", "gemv_moe.hip", "gemv_m34.hip"]
 # the sources of the routed prompt-batch product (sort + fp16 grouped GEMM)
 MOE_GEMM_SOURCES = ["rfp2_device.h", "f16_decode.h", "gemm_f16.hip", "moe_sort.hip"]
+# the sources of the dense prompt-batch products (int8 and fp16 matrix cores)
+GEMM_SOURCES = ["rfp2_device.h", "rfp2_internal.h", "gemm.hip"]
+GEMM_F16_SOURCES = ["rfp2_device.h", "f16_decode.h", "rfp2_internal.h", "gemm_f16.hip"]
 
 
 def kernel_hash(sources=None) -> str:
@@ -599,6 +602,7 @@ def main(argv=None) -> int:
         return 2
 
     r = measure(args.workload, args.steps, args.warmup, args.two_launch, args.per_token)
+    print(f"[bench] {args.workload} measured", file=sys.stderr, flush=True)
     out = {
         "metric": r["metric"], "value": r["value"], "unit": r["unit"], "n_gpus": 1,
         "steps": r["steps"], "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
@@ -609,6 +613,7 @@ def main(argv=None) -> int:
     secondary = []
     for wl in [w for w in args.secondary.split(",") if w and w != args.workload]:
         s = measure(wl, args.steps, args.warmup, args.two_launch, args.per_token)
+        print(f"[bench] {wl} measured", file=sys.stderr, flush=True)
         secondary.append({"workload": wl, "metric": s["metric"], "value": s["value"],
                           "unit": s["unit"], "ms_per_step": s["ms_per_step"],
                           "roofline": {k: s["roofline"][k] for k in

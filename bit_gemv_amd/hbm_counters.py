@@ -10,7 +10,7 @@ runtime's plain device-to-device copy kernel of known size (the bench's
 weight copies); the scale of the largest copies over all runs is used.
 
 Each workload's entry records the hash of the sources of its kernels (the
-GEMV kernels, or those of the routed prompt-batch product); an existing
+GEMV kernels, the routed prompt-batch product or a dense GEMM); an existing
 OUT_JSON keeps its other workloads' entries.
 
 usage: python -m bit_gemv_amd.hbm_counters OUT_JSON WORKLOAD [WORKLOAD ...]
@@ -80,7 +80,7 @@ def main(argv):
             finally:
                 shutil.rmtree(tmp, ignore_errors=True)
         prods = {n: v for n, v in got["FETCH_SIZE"].items()
-                 if "gemv_kernel" in n or "moe_gemm_kernel" in n}
+                 if any(k in n for k in ("gemv_kernel", "gemm_kernel", "gemm_f16_kernel"))}
         kernel = max(prods, key=lambda n: len(prods[n]))
         fetch = statistics.median(got["FETCH_SIZE"][kernel])
         write = statistics.median(got["WRITE_SIZE"][kernel])
@@ -89,7 +89,8 @@ def main(argv):
                 big = [x for x in v if x > 0.9 * max(v)]
                 wv = [x for x in got["WRITE_SIZE"].get(n, []) if x > 0.9 * max(got["WRITE_SIZE"][n])]
                 copies.append((per_copy, statistics.median(big), statistics.median(wv)))
-        sources = bench.MOE_GEMM_SOURCES if cfg["op"] == "moe_gemm" else bench.GEMV_SOURCES
+        sources = {"moe_gemm": bench.MOE_GEMM_SOURCES, "gemm": bench.GEMM_SOURCES,
+                   "gemm_f16": bench.GEMM_F16_SOURCES}.get(cfg["op"], bench.GEMV_SOURCES)
         res[wl] = {"kernel": kernel, "dispatches": len(got["FETCH_SIZE"][kernel]),
                    "fetch_kib_median": fetch, "write_kib_median": write,
                    "algorithmic_bytes_per_launch": alg["product_bytes"],
